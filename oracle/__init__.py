@@ -1,0 +1,19 @@
+"""Float64 CPU oracle of the ARL2 hybrid attention layer.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg; never by the library.
+"""
+from .arl2_oracle import (  # noqa: F401
+    L2_EPS,
+    delta_update,
+    feature_map,
+    frame_forward,
+    head_forward,
+    inter_read,
+    intra_attention,
+    kv_cache_attention,
+    l2_normalize_rows,
+    output_rows,
+    row_softmax,
+    token_level_update,
+)

@@ -1,0 +1,206 @@
+"""Float64 CPU oracle of one ARL2 hybrid attention layer ("Attend Locally,
+Remember Linearly").
+
+TEST INFRASTRUCTURE ONLY. This module is the plain, slow, obviously correct
+definition that the HIP library is checked against. Only the test suite, the
+smoke check and the benchmark's CPU-baseline leg may import it; the library
+itself never calls it and shares no code with it.
+
+Every function below follows a passage of the pages that describe the method:
+
+* [TS] "Technical Summary: Attend Locally, Remember Linearly (ARL2)"
+  (gist.science), section 2.1 "Hybrid Attention Decomposition" and
+  section 2.2 "Memory State Management";
+* [NP] the NeurIPS 2026 poster abstract "Attend Locally, Remember Linearly:
+  Linear Attention as Cross-Frame Memory for Autoregressive Video Diffusion";
+* [AS] the atlas.scime.ai summary of the same paper, sections "Approach",
+  "Surprising findings" and "Builds on" (Gated Delta Network).
+
+Where the pages leave a step open this module takes the plainest reading and
+says so in the function's docstring (softmax scale, no mask, row-vector
+feature maps without bias, the L2 normalisation of Q' and K' with a 1e-6
+floor, the transpose of K' in the update, the plain sum of the branches,
+headwise-scalar alpha and per-token beta).
+
+Arrays are float64; inputs that were stored in bfloat16 or float32 widen to
+float64 exactly, so the oracle sees the same values as the GPU.
+"""
+from __future__ import annotations
+
+import math
+from typing import Tuple
+
+import numpy as np
+
+L2_EPS = 1e-6
+
+
+# ------------------------------------------------------------ intra branch
+def row_softmax(z: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis, shifted by the row maximum for stability."""
+    m = np.max(z, axis=-1, keepdims=True)
+    e = np.exp(z - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def intra_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Intra-frame branch of [TS] section 2.1: full bidirectional softmax
+    attention among the tokens of the current frame, for one head.
+
+    q [Lq][d], k and v [Lk][d] -> [Lq][d]. No mask: every token attends to
+    every token of the frame (bidirectional). The pages do not print the
+    scale; the branch keeps the pretrained softmax attention, so it is the
+    standard scaled dot product with scale 1/sqrt(d).
+
+    The same definition with Lk > Lq is the full-softmax attention over a
+    growing key/value cache that the method replaces ([TS] section 1).
+    """
+    d = q.shape[-1]
+    z = (q @ k.T) / math.sqrt(d)
+    return row_softmax(z) @ v
+
+
+# ------------------------------------------------------------ inter branch
+def feature_map(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Per-head grouped 1x1 feature map of [TS] section 2.1 (phi_q, phi_k,
+    phi_v): one d x d linear map per head applied to every token.
+
+    Reading: row-vector convention x' = x W with W stored [d_in][d_out], no
+    bias (the pages give neither an orientation nor a bias).
+    """
+    return x @ W
+
+
+def l2_normalize_rows(x: np.ndarray, eps: float = L2_EPS) -> np.ndarray:
+    """Scale every token's vector to unit Euclidean length.
+
+    Not on the pages: this implementation's stated choice for Q' and K'.
+    A row of norm below ``eps`` is divided by ``eps`` (a zero row stays zero).
+    """
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)
+
+
+def inter_read(Qp: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """Inter-frame read of [TS] section 2.1: O_inter = Q'_N S_{N-1}.
+
+    Qp [L][d_k], S [d_k][d_v] -> [L][d_v]. Every token of the frame reads the
+    same pre-update state (frame-level access, [TS] section 2.2).
+    """
+    return Qp @ S
+
+
+def delta_update(S: np.ndarray, Kp: np.ndarray, Vp: np.ndarray, alpha: float,
+                 beta: np.ndarray) -> np.ndarray:
+    """Gated delta state update of [TS] section 2.1, one frame:
+
+        R   = V' - K' S_{N-1}                     (residual of every token)
+        S_N = alpha S_{N-1} + K'^T diag(beta) R
+
+    S [d_k][d_v], Kp [L][d_k], Vp [L][d_v], alpha a scalar (headwise gate of
+    this frame), beta [L] (one learning rate per token). The printed formula
+    omits the transpose; with tokens as rows of K' the product that yields a
+    d_k x d_v matrix is K'^T (...). Returns the new state (a new array).
+    """
+    R = Vp - Kp @ S
+    return alpha * S + Kp.T @ (beta[:, None] * R)
+
+
+def token_level_update(S: np.ndarray, Kp: np.ndarray, Vp: np.ndarray, alpha: float,
+                       beta: np.ndarray) -> np.ndarray:
+    """The token-level access that the pages' ablation compares against
+    ([TS] section 4, [AS] "Surprising findings"): tokens of the frame write
+    the state one after another, each applying the update of [TS] section 2.1
+    with a single token,
+        S_i = a_i S_{i-1} + beta_i k_i (v_i - k_i^T S_{i-1}),
+    where the frame's forget gate is applied with the first token only
+    (a_1 = alpha, a_i = 1 after it), so that a one-token frame gives the
+    frame-level result. Used only to show that frame-level access differs
+    from it.
+    """
+    for i in range(Kp.shape[0]):
+        k = Kp[i]
+        a = alpha if i == 0 else 1.0
+        S = a * S + beta[i] * np.outer(k, Vp[i] - k @ S)
+    return S
+
+
+# ------------------------------------------------------------ one layer
+def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, Wq: np.ndarray,
+                 Wk: np.ndarray, Wv: np.ndarray, S: np.ndarray, alpha: float,
+                 beta: np.ndarray, update: bool) -> Tuple[np.ndarray, np.ndarray]:
+    """One pass of one head of one stream.
+
+    out = O_intra + O_inter: the pages say the layer splits attention into the
+    two branches but not how they are merged; the plain sum is this
+    implementation's reading. O_inter reads the pre-update state; only a clean
+    pass (``update``) produces S_N ([TS] section 2.2). Returns (out, S_next);
+    S_next is S itself when no update happens.
+    """
+    o_intra = intra_attention(q, k, v)
+    Qp = l2_normalize_rows(feature_map(q, Wq))
+    out = o_intra + inter_read(Qp, S)
+    if not update:
+        return out, S
+    Kp = l2_normalize_rows(feature_map(k, Wk))
+    Vp = feature_map(v, Wv)
+    return out, delta_update(S, Kp, Vp, alpha, beta)
+
+
+def frame_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, Wphi: np.ndarray,
+                  S: np.ndarray, alpha, beta, update_flag: int) -> np.ndarray:
+    """One pass of the layer over a batch of streams.
+
+    q, k, v [B][L][H][d] (token-major); Wphi [3][H][d][d] (maps for q, k, v);
+    S [B][H][d][d] float64, updated IN PLACE when ``update_flag`` is 1 and
+    left untouched when it is 0 ([TS] section 2.2: denoising passes only
+    read, the clean pass writes); alpha [B][H]; beta [B][L][H].
+    Returns out [B][L][H][d] float64.
+    """
+    assert update_flag in (0, 1)
+    B, L, H, d = q.shape
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    W = np.asarray(Wphi, dtype=np.float64)
+    out = np.empty((B, L, H, d), dtype=np.float64)
+    new_states = {}
+    for b in range(B):
+        for h in range(H):
+            a = float(alpha[b][h]) if update_flag else 0.0
+            be = np.asarray(beta[b][:, h], dtype=np.float64) if update_flag else None
+            o, s_next = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], W[0, h], W[1, h],
+                                     W[2, h], S[b, h], a, be, bool(update_flag))
+            out[b, :, h] = o
+            if update_flag:
+                new_states[(b, h)] = s_next
+    # Every head of the frame read the pre-update state above; write after.
+    for (b, h), s_next in new_states.items():
+        S[b, h] = s_next
+    return out
+
+
+def output_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, Wq: np.ndarray,
+                S: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """out for a subset of query rows of one head (the same definition as
+    ``head_forward``, restricted to the requested rows; used to check large
+    workloads on sampled outputs). q/k/v [L][d], S [d][d] pre-update."""
+    qs = np.asarray(q, dtype=np.float64)[rows]
+    o_intra = intra_attention(qs, np.asarray(k, np.float64), np.asarray(v, np.float64))
+    Qp = l2_normalize_rows(feature_map(qs, np.asarray(Wq, np.float64)))
+    return o_intra + inter_read(Qp, S)
+
+
+def kv_cache_attention(q: np.ndarray, kc: np.ndarray, vc: np.ndarray) -> np.ndarray:
+    """Full-softmax attention of one frame's queries over a key/value cache,
+    per stream and head: q [B][Lq][H][d], kc/vc [B][Lk][H][d] -> [B][Lq][H][d].
+    This is the attention whose growing cache the method removes ([TS]
+    section 1); it is the same definition as ``intra_attention``."""
+    B, Lq, H, d = q.shape
+    out = np.empty((B, Lq, H, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            out[b, :, h] = intra_attention(np.asarray(q[b, :, h], np.float64),
+                                           np.asarray(kc[b, :, h], np.float64),
+                                           np.asarray(vc[b, :, h], np.float64))
+    return out

@@ -1,0 +1,367 @@
+// C ABI of libarl2 (include/arl2.h): argument validation, workspace layout
+// and the launch sequence of one ARL2 layer pass.
+//
+// Pass structure ("Technical Summary: Attend Locally, Remember Linearly
+// (ARL2)", section 2.2): every pass computes out = O_intra + Q' S_{N-1};
+// only the clean pass (update_flag = 1) then updates S. In stream order:
+//   1. intra-frame attention partials over key ranges   -> workspace
+//   2. merge partials + Q' = L2norm(q W_q), O_inter = Q'S -> out
+//   3. (clean pass) per-chunk dS_c = K'^T diag(beta)(V' - K'S) -> workspace
+//   4. (clean pass) S = alpha S + sum_c dS_c
+// Step 2 reads S before step 3 and 4 run, so every token of the frame reads
+// the pre-update state.
+#include "arl2.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "arl2_kernels.h"
+
+namespace {
+
+constexpr int32_t kMagic = 0x41524c32;  // "ARL2"
+constexpr int64_t kMaxH = 65535;
+constexpr int64_t kMaxB = 65535;
+
+thread_local char g_err[512] = "";
+
+arl2_status fail(arl2_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+arl2_status fail(arl2_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+arl2_status ok() {
+  g_err[0] = 0;
+  return ARL2_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range(const void *p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+size_t esize(int32_t dtype) { return dtype == ARL2_BF16 ? 2 : 4; }
+
+bool mfma_path(int32_t d, int32_t dtype) { return d == ARL2_D_LARGE && dtype == ARL2_BF16; }
+
+arl2_status check_shape(int64_t B, int64_t H, int64_t d, int64_t L, int64_t dtype,
+                        const char *what) {
+  if (dtype != ARL2_BF16 && dtype != ARL2_F32)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: dtype %lld is not ARL2_BF16 or ARL2_F32", what,
+                (long long)dtype);
+  if (B < 1 || B > kMaxB || H < 1 || H > kMaxH || L < 1 || L > ARL2_MAX_L || d < 1)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: bad shape B=%lld H=%lld d=%lld L=%lld", what,
+                (long long)B, (long long)H, (long long)d, (long long)L);
+  if (d != ARL2_D_SMALL && d != ARL2_D_LARGE)
+    return fail(ARL2_ERR_UNSUPPORTED, "%s: head dimension %lld (supported: 16, 128)", what,
+                (long long)d);
+  if (B * L * H * d > ((int64_t)1 << 40))
+    return fail(ARL2_ERR_INVALID_ARG, "%s: tensor of B*L*H*d = %lld elements is too large", what,
+                (long long)(B * L * H * d));
+  return ARL2_OK;
+}
+
+// Workspace layout of arl2_frame_forward.
+struct FramePlan {
+  bool mfma = false;
+  arl2::AttnPlan ap;
+  int nchunk = 0;
+  size_t off_o = 0, off_ml = 0, off_ds = 0, total = 0;
+};
+
+FramePlan plan_frame(int64_t B, int64_t H, int64_t d, int64_t L, int32_t dtype) {
+  FramePlan fp;
+  fp.mfma = mfma_path((int32_t)d, dtype);
+  size_t o_bytes, ml_bytes;
+  if (fp.mfma) {
+    fp.ap = arl2::plan_attention(B, H, L, L);
+    const size_t blocks = (size_t)B * H * fp.ap.nqblk * fp.ap.nsplit;
+    o_bytes = blocks * arl2::kPartialO * sizeof(float);
+    ml_bytes = blocks * arl2::kPartialML * sizeof(float);
+    fp.nchunk = (int)((L + arl2::kDeltaChunk - 1) / arl2::kDeltaChunk);
+  } else {
+    o_bytes = (size_t)B * H * L * d * sizeof(float);
+    ml_bytes = 0;
+    fp.nchunk = (int)((L + arl2::kGenChunk - 1) / arl2::kGenChunk);
+  }
+  const size_t ds_bytes = (size_t)B * H * fp.nchunk * d * d * sizeof(float);
+  fp.off_o = 0;
+  fp.off_ml = align256(o_bytes);
+  fp.off_ds = fp.off_ml + align256(ml_bytes);
+  fp.total = fp.off_ds + align256(ds_bytes);
+  return fp;
+}
+
+struct AttnOnlyPlan {
+  bool mfma = false;
+  arl2::AttnPlan ap;
+  size_t off_o = 0, off_ml = 0, total = 0;
+};
+
+AttnOnlyPlan plan_attn_only(int64_t B, int64_t H, int64_t d, int64_t Lq, int64_t Lk,
+                            int32_t dtype) {
+  AttnOnlyPlan p;
+  p.mfma = mfma_path((int32_t)d, dtype);
+  size_t o_bytes, ml_bytes = 0;
+  if (p.mfma) {
+    p.ap = arl2::plan_attention(B, H, Lq, Lk);
+    const size_t blocks = (size_t)B * H * p.ap.nqblk * p.ap.nsplit;
+    o_bytes = blocks * arl2::kPartialO * sizeof(float);
+    ml_bytes = blocks * arl2::kPartialML * sizeof(float);
+  } else {
+    o_bytes = (size_t)B * H * Lq * d * sizeof(float);
+  }
+  p.off_o = 0;
+  p.off_ml = align256(o_bytes);
+  p.total = p.off_ml + align256(ml_bytes);
+  return p;
+}
+
+arl2_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ARL2_OK;
+  return fail(ARL2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t arl2_version(void) { return ARL2_VERSION; }
+
+const char *arl2_status_string(int32_t status) {
+  switch (status) {
+    case ARL2_OK: return "ok";
+    case ARL2_ERR_INVALID_ARG: return "invalid argument";
+    case ARL2_ERR_UNSUPPORTED: return "unsupported";
+    case ARL2_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *arl2_last_error(void) { return g_err; }
+
+size_t arl2_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t L, int32_t dtype) {
+  if (check_shape(B, H, d, L, dtype, "arl2_workspace_bytes") != ARL2_OK) return 0;
+  return plan_frame(B, H, d, L, dtype).total;
+}
+
+arl2_status arl2_state_init(arl2_state *st, int32_t B, int32_t H, int32_t d, int32_t L,
+                            int32_t dtype, float *S_dev, void *ws_dev, size_t ws_bytes,
+                            void *stream) {
+  if (!st) return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: st is NULL");
+  arl2_status cs = check_shape(B, H, d, L, dtype, "arl2_state_init");
+  if (cs != ARL2_OK) return cs;
+  if (!S_dev) return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: S_dev is NULL");
+  if (!aligned(S_dev, 16))
+    return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: S_dev is not 16-byte aligned");
+  const size_t need = plan_frame(B, H, d, L, dtype).total;
+  if (ws_bytes < need)
+    return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: workspace of %zu bytes, need %zu",
+                ws_bytes, need);
+  if (need > 0 && !ws_dev) return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: ws_dev is NULL");
+  if (ws_dev && !aligned(ws_dev, 256))
+    return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: ws_dev is not 256-byte aligned");
+  const size_t s_bytes = (size_t)B * H * d * d * sizeof(float);
+  if (ws_dev && overlap(range(S_dev, s_bytes), range(ws_dev, ws_bytes)))
+    return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: S and workspace overlap");
+  arl2_status hs = hip_status(
+      arl2::launch_fill_state(S_dev, nullptr, (int64_t)B * H * d * d, (hipStream_t)stream),
+      "arl2_state_init");
+  if (hs != ARL2_OK) return hs;
+  st->B = B;
+  st->H = H;
+  st->d = d;
+  st->L = L;
+  st->dtype = dtype;
+  st->magic = kMagic;
+  st->S = S_dev;
+  st->ws = ws_dev;
+  st->ws_bytes = ws_bytes;
+  return ok();
+}
+
+static arl2_status check_state(const arl2_state *st, const char *what) {
+  if (!st) return fail(ARL2_ERR_INVALID_ARG, "%s: st is NULL", what);
+  if (st->magic != kMagic || !st->S)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: state was not set up by arl2_state_init", what);
+  arl2_status cs = check_shape(st->B, st->H, st->d, st->L, st->dtype, what);
+  if (cs != ARL2_OK) return cs;
+  if (st->ws_bytes < plan_frame(st->B, st->H, st->d, st->L, st->dtype).total)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: workspace too small for the state's shape", what);
+  return ARL2_OK;
+}
+
+arl2_status arl2_state_reset(arl2_state *st, const float *S0_dev, void *stream) {
+  arl2_status cs = check_state(st, "arl2_state_reset");
+  if (cs != ARL2_OK) return cs;
+  const int64_t n = (int64_t)st->B * st->H * st->d * st->d;
+  if (S0_dev) {
+    if (!aligned(S0_dev, 4))
+      return fail(ARL2_ERR_INVALID_ARG, "arl2_state_reset: S0 is misaligned");
+    if (overlap(range(S0_dev, n * sizeof(float)), range(st->S, n * sizeof(float))))
+      return fail(ARL2_ERR_INVALID_ARG, "arl2_state_reset: S0 overlaps S");
+  }
+  arl2_status hs = hip_status(arl2::launch_fill_state(st->S, S0_dev, n, (hipStream_t)stream),
+                              "arl2_state_reset");
+  if (hs != ARL2_OK) return hs;
+  return ok();
+}
+
+arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, const void *Wphi,
+                               arl2_state *st, const float *alpha, const float *beta, void *out,
+                               int32_t update_flag, void *stream) {
+  const char *fn = "arl2_frame_forward";
+  arl2_status cs = check_state(st, fn);
+  if (cs != ARL2_OK) return cs;
+  if (update_flag != 0 && update_flag != 1)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: update_flag %d is not 0 or 1", fn, update_flag);
+  const void *tens[5] = {q, k, v, Wphi, out};
+  const char *names[5] = {"q", "k", "v", "Wphi", "out"};
+  for (int i = 0; i < 5; ++i) {
+    if (!tens[i]) return fail(ARL2_ERR_INVALID_ARG, "%s: %s is NULL", fn, names[i]);
+    if (!aligned(tens[i], 16))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  const int64_t B = st->B, H = st->H, d = st->d, L = st->L;
+  const size_t es = esize(st->dtype);
+  const size_t act = (size_t)B * L * H * d * es;
+  const size_t wbytes = (size_t)3 * H * d * d * es;
+  const size_t sbytes = (size_t)B * H * d * d * sizeof(float);
+  const Range r_out = range(out, act), r_S = range(st->S, sbytes),
+              r_ws = range(st->ws, st->ws_bytes);
+  const Range r_in[4] = {range(q, act), range(k, act), range(v, act), range(Wphi, wbytes)};
+  for (int i = 0; i < 4; ++i)
+    if (overlap(r_out, r_in[i]))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: out overlaps %s", fn, names[i]);
+  if (overlap(r_out, r_S) || overlap(r_out, r_ws))
+    return fail(ARL2_ERR_INVALID_ARG, "%s: out overlaps the state or its workspace", fn);
+  for (int i = 0; i < 4; ++i)
+    if (overlap(r_ws, r_in[i]) || overlap(r_S, r_in[i]))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: %s overlaps the state or its workspace", fn,
+                  names[i]);
+  if (update_flag) {
+    if (!alpha || !beta)
+      return fail(ARL2_ERR_INVALID_ARG, "%s: alpha and beta are required when update_flag == 1",
+                  fn);
+    if (!aligned(alpha, 4) || !aligned(beta, 4))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: alpha/beta are misaligned", fn);
+    const Range r_a = range(alpha, (size_t)B * H * 4), r_b = range(beta, (size_t)B * L * H * 4);
+    if (overlap(r_a, r_S) || overlap(r_b, r_S) || overlap(r_a, r_ws) || overlap(r_b, r_ws))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: alpha/beta overlap the state or its workspace", fn);
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const FramePlan fp = plan_frame(B, H, d, L, st->dtype);
+  char *ws = (char *)st->ws;
+  float *ws_o = (float *)(ws + fp.off_o);
+  float *ws_ml = (float *)(ws + fp.off_ml);
+  float *ws_ds = (float *)(ws + fp.off_ds);
+  const char *wbase = (const char *)Wphi;
+  const void *Wq = wbase;
+  const void *Wk = wbase + (size_t)H * d * d * es;
+  const void *Wv = wbase + (size_t)2 * H * d * d * es;
+
+  hipError_t e;
+  if (fp.mfma) {
+    arl2::AttnArgs aa{q, k, v, (int)B, (int)H, (int)L, (int)L, fp.ap, ws_o, ws_ml};
+    if ((e = arl2::launch_attn_partial_bf16(aa, s)) != hipSuccess) return hip_status(e, fn);
+    arl2::CombineArgs ca{q, Wq, st->S, (int)B, (int)H, (int)L, fp.ap, ws_o, ws_ml, out, true};
+    if ((e = arl2::launch_inter_combine_bf16(ca, s)) != hipSuccess) return hip_status(e, fn);
+    if (update_flag) {
+      arl2::DeltaArgs da{k, v, Wk, Wv, st->S, beta, (int)B, (int)H, (int)L, fp.nchunk, ws_ds};
+      if ((e = arl2::launch_delta_partial_bf16(da, s)) != hipSuccess) return hip_status(e, fn);
+    }
+  } else {
+    if ((e = arl2::launch_generic_attention(st->dtype, (int)d, q, k, v, (int)B, (int)H, (int)L,
+                                            (int)L, ws_o, s)) != hipSuccess)
+      return hip_status(e, fn);
+    if ((e = arl2::launch_generic_inter_combine(st->dtype, (int)d, q, Wq, st->S, ws_o, (int)B,
+                                                (int)H, (int)L, out, true, s)) != hipSuccess)
+      return hip_status(e, fn);
+    if (update_flag) {
+      if ((e = arl2::launch_generic_delta_partial(st->dtype, (int)d, k, v, Wk, Wv, st->S, beta,
+                                                  (int)B, (int)H, (int)L, ws_ds, s)) != hipSuccess)
+        return hip_status(e, fn);
+    }
+  }
+  if (update_flag) {
+    if ((e = arl2::launch_delta_apply(st->S, alpha, ws_ds, (int)B, (int)H, (int)d, fp.nchunk,
+                                      s)) != hipSuccess)
+      return hip_status(e, fn);
+  }
+  return ok();
+}
+
+size_t arl2_softmax_attention_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t Lq,
+                                              int32_t Lk, int32_t dtype) {
+  if (check_shape(B, H, d, Lq, dtype, "arl2_softmax_attention_workspace_bytes") != ARL2_OK ||
+      check_shape(B, H, d, Lk, dtype, "arl2_softmax_attention_workspace_bytes") != ARL2_OK)
+    return 0;
+  return plan_attn_only(B, H, d, Lq, Lk, dtype).total;
+}
+
+arl2_status arl2_softmax_attention(const void *q, const void *kc, const void *vc, int32_t B,
+                                   int32_t H, int32_t d, int32_t Lq, int32_t Lk, int32_t dtype,
+                                   void *out, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "arl2_softmax_attention";
+  arl2_status cs = check_shape(B, H, d, Lq, dtype, fn);
+  if (cs != ARL2_OK) return cs;
+  cs = check_shape(B, H, d, Lk, dtype, fn);
+  if (cs != ARL2_OK) return cs;
+  const void *tens[4] = {q, kc, vc, out};
+  const char *names[4] = {"q", "kc", "vc", "out"};
+  for (int i = 0; i < 4; ++i) {
+    if (!tens[i]) return fail(ARL2_ERR_INVALID_ARG, "%s: %s is NULL", fn, names[i]);
+    if (!aligned(tens[i], 16))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  const AttnOnlyPlan ap = plan_attn_only(B, H, d, Lq, Lk, dtype);
+  if (ws_bytes < ap.total)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: workspace of %zu bytes, need %zu", fn, ws_bytes,
+                ap.total);
+  if (!ws || !aligned(ws, 256))
+    return fail(ARL2_ERR_INVALID_ARG, "%s: ws is NULL or not 256-byte aligned", fn);
+  const size_t es = esize(dtype);
+  const Range r_out = range(out, (size_t)B * Lq * H * d * es);
+  const Range r_in[3] = {range(q, (size_t)B * Lq * H * d * es),
+                         range(kc, (size_t)B * Lk * H * d * es),
+                         range(vc, (size_t)B * Lk * H * d * es)};
+  const Range r_ws = range(ws, ws_bytes);
+  for (int i = 0; i < 3; ++i)
+    if (overlap(r_out, r_in[i]) || overlap(r_ws, r_in[i]))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: %s overlaps out or the workspace", fn, names[i]);
+  if (overlap(r_out, r_ws)) return fail(ARL2_ERR_INVALID_ARG, "%s: out overlaps ws", fn);
+
+  hipStream_t s = (hipStream_t)stream;
+  float *ws_o = (float *)((char *)ws + ap.off_o);
+  float *ws_ml = (float *)((char *)ws + ap.off_ml);
+  hipError_t e;
+  if (ap.mfma) {
+    arl2::AttnArgs aa{q, kc, vc, B, H, Lq, Lk, ap.ap, ws_o, ws_ml};
+    if ((e = arl2::launch_attn_partial_bf16(aa, s)) != hipSuccess) return hip_status(e, fn);
+    arl2::CombineArgs ca{q, nullptr, nullptr, B, H, Lq, ap.ap, ws_o, ws_ml, out, false};
+    if ((e = arl2::launch_inter_combine_bf16(ca, s)) != hipSuccess) return hip_status(e, fn);
+  } else {
+    if ((e = arl2::launch_generic_attention(dtype, d, q, kc, vc, B, H, Lq, Lk, ws_o, s)) !=
+        hipSuccess)
+      return hip_status(e, fn);
+    if ((e = arl2::launch_generic_inter_combine(dtype, d, q, nullptr, nullptr, ws_o, B, H, Lq,
+                                                out, false, s)) != hipSuccess)
+      return hip_status(e, fn);
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Device helpers shared by the libarl2 kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace arl2 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kL2Eps = 1e-6f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// D(32x32) += A(32x16) * B(16x32) on the matrix cores, bf16 operands, fp32
+// accumulation. Lane l supplies A[row = l%32][k = 8*(l/32) .. +7] and
+// B[k = 8*(l/32) .. +7][col = l%32]; the accumulator register i of lane l
+// holds D[row = 8*(i/4) + 4*(l/32) + i%4][col = l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Accumulator rows come in the order 8*(i/4) + 4*(l/32) + i%4; an operand's
+// k index runs 8*(l/32) + j. Within a group of 16, row r of an accumulator
+// therefore lines up with operand position swap_bits23(r): registers
+// 8*g2 .. 8*g2+7 of an accumulator can be fed to the next MFMA as its k
+// operand unchanged, provided the other operand stores its k dimension in
+// this permuted order. The map is an involution.
+__device__ __host__ __forceinline__ constexpr int swap_bits23(int p) {
+  return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.f;
+  return z;
+}
+
+// True if the predicate holds on any lane of the wavefront.
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exchange with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// Split an fp32 value into bf16 high and low parts, x ~= hi + lo (the
+// three-product bf16 scheme of Henry, Tang and Heinecke, ARITH 2019).
+__device__ __forceinline__ void split_bf16(float x, bf16 &hi, bf16 &lo) {
+  hi = (bf16)x;
+  lo = (bf16)(x - (float)hi);
+}
+
+}  // namespace arl2

@@ -1,0 +1,87 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+// Not installed; the public interface is include/arl2.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace arl2 {
+
+// ---------------------------------------------------------------- plans
+// How one attention call is cut into workgroups: query blocks of 128 rows
+// (4 wavefronts x 32 queries) and `nsplit` contiguous key ranges of
+// `keys_per_split` keys (a multiple of the 64-key tile). Partial results of
+// the key ranges are merged by the combine kernel.
+struct AttnPlan {
+  int nqblk = 0;
+  int nsplit = 0;
+  int keys_per_split = 0;
+};
+
+constexpr int kQBlock = 128;      // queries per attention workgroup
+constexpr int kKeyTile = 64;      // keys per LDS tile
+constexpr int kDeltaChunk = 128;  // tokens per delta-update workgroup (MFMA path)
+constexpr int kGenChunk = 32;     // tokens per delta-update workgroup (generic path)
+
+AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk);
+
+// Floats of partial output per (stream, head, query block, split): 4 waves x
+// 64 accumulator registers x 64 lanes; and of row statistics (max, sum).
+constexpr int64_t kPartialO = 4 * 64 * 64;
+constexpr int64_t kPartialML = 4 * 64;
+
+// ---------------------------------------------------------------- MFMA path
+// bf16 io, d = 128.
+struct AttnArgs {
+  const void *q, *k, *v;  // [B][Lq][H][128], [B][Lk][H][128]
+  int B, H, Lq, Lk;
+  AttnPlan plan;
+  float *ws_o, *ws_ml;
+};
+hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s);
+
+struct CombineArgs {
+  const void *q;     // [B][L][H][128] (read only when with_inter)
+  const void *Wq;    // [H][128][128]
+  const float *S;    // [B][H][128][128]
+  int B, H, L;
+  AttnPlan plan;
+  const float *ws_o, *ws_ml;
+  void *out;         // [B][L][H][128]
+  bool with_inter;
+};
+hipError_t launch_inter_combine_bf16(const CombineArgs &a, hipStream_t s);
+
+struct DeltaArgs {
+  const void *k, *v;     // [B][L][H][128]
+  const void *Wk, *Wv;   // [H][128][128]
+  const float *S;        // [B][H][128][128] (pre-update, read only)
+  const float *beta;     // [B][L][H]
+  int B, H, L, nchunk;
+  float *ws_dS;          // [B][H][nchunk][128][128]
+};
+hipError_t launch_delta_partial_bf16(const DeltaArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- shared
+// S[b][h] := alpha[b][h] * S[b][h] + sum over chunks c (in order) of
+// ws_dS[b][h][c], elementwise.
+hipError_t launch_delta_apply(float *S, const float *alpha, const float *ws_dS, int B, int H,
+                              int d, int nchunk, hipStream_t s);
+// dst[i] := src ? src[i] : 0 for i < n.
+hipError_t launch_fill_state(float *dst, const float *src, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- generic path
+// Any dtype, d in {16, 128}: plain VALU kernels for the small fp32 workloads.
+// dtype: 0 = bf16, 1 = f32 (arl2_dtype).
+hipError_t launch_generic_attention(int dtype, int d, const void *q, const void *k, const void *v,
+                                    int B, int H, int Lq, int Lk, float *o_intra, hipStream_t s);
+hipError_t launch_generic_inter_combine(int dtype, int d, const void *q, const void *Wq,
+                                        const float *S, const float *o_intra, int B, int H, int L,
+                                        void *out, bool with_inter, hipStream_t s);
+hipError_t launch_generic_delta_partial(int dtype, int d, const void *k, const void *v,
+                                        const void *Wk, const void *Wv, const float *S,
+                                        const float *beta, int B, int H, int L, float *ws_dS,
+                                        hipStream_t s);
+
+}  // namespace arl2

@@ -1,0 +1,43 @@
+"""Device buffers for one ARL2 layer, allocated by torch, driven through the
+C ABI. Torch is used for memory and streams only; every step of the layer
+runs in libarl2's kernels."""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+TORCH_DTYPE = {B.ARL2_BF16: torch.bfloat16, B.ARL2_F32: torch.float32}
+
+
+class ARL2Layer:
+    """State S [B][H][d][d] fp32 plus the workspace of one layer."""
+
+    def __init__(self, Bn: int, H: int, d: int, L: int, dtype: int, device="cuda", stream=None):
+        self.shape = (Bn, H, d, L)
+        self.dtype = dtype
+        self.S = torch.empty((Bn, H, d, d), dtype=torch.float32, device=device)
+        self.ws_bytes = B.arl2_workspace_bytes(Bn, H, d, L, dtype)
+        if self.ws_bytes == 0:
+            raise ValueError(f"invalid layer shape {self.shape}")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.st = B.arl2_state()
+        B.arl2_state_init(self.st, Bn, H, d, L, dtype, self.S, self.ws, self.ws_bytes, stream)
+
+    def reset(self, S0=None, stream=None) -> None:
+        B.arl2_state_reset(self.st, S0, stream)
+
+    def forward(self, q, k, v, W, alpha, beta, out, update: bool, stream=None) -> None:
+        B.arl2_frame_forward(q, k, v, W, self.st, alpha, beta, out, 1 if update else 0, stream)
+
+
+def softmax_attention(q, kc, vc, out, dtype: int, ws=None, stream=None):
+    """Full-softmax attention over a key/value cache (the comparator);
+    allocates the workspace with torch when none is given."""
+    Bn, Lq, H, d = q.shape
+    Lk = kc.shape[1]
+    nb = B.arl2_softmax_attention_workspace_bytes(Bn, H, d, Lq, Lk, dtype)
+    if ws is None or ws.numel() < nb:
+        ws = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    B.arl2_softmax_attention(q, kc, vc, Bn, H, d, Lq, Lk, dtype, out, ws, nb, stream)
+    return ws

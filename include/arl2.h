@@ -1,0 +1,171 @@
+/*
+ * libarl2 — one ARL2 ("Attend Locally, Remember Linearly") hybrid attention
+ * layer on AMD Instinct MI355X (gfx950).
+ *
+ * The method (see "Technical Summary: Attend Locally, Remember Linearly
+ * (ARL2)", gist.science, section 2.1 "Hybrid Attention Decomposition" and
+ * section 2.2 "Memory State Management") splits a video DiT's self-attention
+ * into two branches per head:
+ *
+ *   intra-frame: softmax attention among the L tokens of the current frame,
+ *                bidirectional (no mask), scale 1/sqrt(d);
+ *   inter-frame: a fixed-size state S (d_k x d_v, fp32, per stream and head)
+ *                read through feature-mapped queries, O_inter = Q' S_{N-1},
+ *                and written once per frame by the gated delta rule
+ *                S_N = alpha S_{N-1} + K'^T diag(beta) (V' - K' S_{N-1}).
+ *
+ * Q' = L2norm(q W_q), K' = L2norm(k W_k), V' = v W_v (per-head d x d maps,
+ * row-vector convention x' = x W, no bias; the L2 normalisation, with a
+ * 1e-6 floor on the norm, is this library's choice — the pages do not state
+ * one). The layer output is the plain sum out = O_intra + O_inter.
+ * Every token of a frame reads the same pre-update state (frame-level
+ * access); noisy denoising passes only read S, and only the final clean pass
+ * of a frame updates it (clean-pass updates).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the
+ *    library never allocates device memory, never frees caller memory and
+ *    keeps no pointer beyond the arl2_state descriptor the caller owns.
+ *  - Activations use token-major layout [B][L][H][d], contiguous.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously; kernel faults surface at the caller's
+ *    next synchronisation of that stream.
+ *  - Every argument is validated before anything is enqueued. On any error
+ *    nothing is written and nothing is launched.
+ *  - Calls on different states may run concurrently on different streams.
+ *    Two calls that share one state (its S or its workspace) must be
+ *    ordered by the caller (same stream, or events).
+ *  - Results are bitwise reproducible run to run: no floating-point atomics.
+ */
+#ifndef ARL2_H
+#define ARL2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ARL2_API __attribute__((visibility("default")))
+#else
+#define ARL2_API
+#endif
+
+#define ARL2_VERSION 1
+
+typedef enum {
+  ARL2_OK = 0,
+  ARL2_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, bad size or flag     */
+  ARL2_ERR_UNSUPPORTED = 2, /* a valid request this build does not handle    */
+  ARL2_ERR_HIP = 3          /* the HIP runtime refused a launch or a copy    */
+} arl2_status;
+
+typedef enum {
+  ARL2_BF16 = 0, /* q, k, v, W_phi, out stored as bfloat16 */
+  ARL2_F32 = 1   /* q, k, v, W_phi, out stored as float32  */
+} arl2_dtype;
+
+/* Head dimensions this build supports (d_k = d_v = d). */
+#define ARL2_D_SMALL 16
+#define ARL2_D_LARGE 128
+
+/* Largest tokens-per-frame value accepted (keeps every index in int32). */
+#define ARL2_MAX_L (1 << 20)
+
+/*
+ * Per-layer state descriptor. Plain data; the caller owns it and the buffers
+ * it points to. Filled by arl2_state_init; do not modify its fields after.
+ */
+typedef struct {
+  int32_t B;        /* independent streams (batch)                          */
+  int32_t H;        /* heads                                                 */
+  int32_t d;        /* head dimension: 16 or 128                             */
+  int32_t L;        /* tokens per frame (fixed for the life of the state)    */
+  int32_t dtype;    /* arl2_dtype of the io tensors                          */
+  int32_t magic;    /* set by arl2_state_init; marks the descriptor as bound */
+  float *S;         /* device, [B][H][d][d] fp32, row = d_k, column = d_v    */
+  void *ws;         /* device workspace of ws_bytes bytes                    */
+  size_t ws_bytes;
+} arl2_state;
+
+/*
+ * Bytes of device workspace arl2_frame_forward needs for this shape.
+ * Returns 0 for an invalid shape. The workspace holds partial results of the
+ * split attention and of the split state update between kernels; its size
+ * does not depend on the number of frames.
+ */
+ARL2_API size_t arl2_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t L, int32_t dtype);
+
+/*
+ * Bind a state to caller-owned device memory and set S := 0.
+ *   S_dev   device [B][H][d][d] float32, 16-byte aligned.
+ *   ws_dev  device workspace of at least arl2_workspace_bytes(...) bytes,
+ *           256-byte aligned (may be NULL only if that size is 0).
+ * The zero fill is enqueued on `stream`.
+ * Errors: INVALID_ARG for NULL st/S_dev, a bad shape, a too-small or
+ * misaligned workspace; UNSUPPORTED for d not in {16, 128}.
+ */
+ARL2_API arl2_status arl2_state_init(arl2_state *st, int32_t B, int32_t H, int32_t d, int32_t L,
+                            int32_t dtype, float *S_dev, void *ws_dev, size_t ws_bytes,
+                            void *stream);
+
+/*
+ * Start a new video stream on an initialised state: S := S0 (device,
+ * [B][H][d][d] float32, may not alias S), or S := 0 when S0_dev is NULL.
+ * Restoring a saved S this way resumes a stream exactly where it was.
+ */
+ARL2_API arl2_status arl2_state_reset(arl2_state *st, const float *S0_dev, void *stream);
+
+/*
+ * One pass of one frame through the layer.
+ *   q, k, v  device [B][L][H][d], io dtype, 16-byte aligned, not aliasing out.
+ *   Wphi     device [3][H][d][d], io dtype: the maps for q, k, v; map[m][h]
+ *            is stored [d_in][d_out] and applied as x' = x W.
+ *   st       state from arl2_state_init (shape taken from it).
+ *   alpha    device [B][H] float32: this frame's forget gate, one scalar per
+ *            stream and head. Read only when update_flag == 1 (may be NULL
+ *            when update_flag == 0).
+ *   beta     device [B][L][H] float32: this frame's per-token learning rate.
+ *            Same NULL rule as alpha.
+ *   out      device [B][L][H][d], io dtype: O_intra + O_inter, rounded to the
+ *            io dtype (round to nearest even).
+ *   update_flag 0 = noisy (query-only) pass: S is not touched.
+ *               1 = clean pass: out is computed from the pre-update S, then
+ *                   S is updated in place, in stream order.
+ * Errors: INVALID_ARG for NULL/misaligned pointers, aliasing of out with an
+ * input, update_flag not in {0, 1}, NULL alpha/beta with update_flag == 1,
+ * or an uninitialised state; ARL2_ERR_HIP if a launch fails.
+ */
+ARL2_API arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, const void *Wphi,
+                               arl2_state *st, const float *alpha, const float *beta,
+                               void *out, int32_t update_flag, void *stream);
+
+/*
+ * Full-softmax attention of Lq queries over Lk cached keys/values per stream
+ * and head, with scale 1/sqrt(d) and no mask: the growing key/value-cache
+ * attention that the method replaces ("Technical Summary ...", section 1,
+ * KV cache growth). Same kernels as the intra-frame branch.
+ *   q   device [B][Lq][H][d];  kc, vc device [B][Lk][H][d];  out [B][Lq][H][d]
+ *   ws  device workspace of arl2_softmax_attention_workspace_bytes(...) bytes.
+ */
+ARL2_API size_t arl2_softmax_attention_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t Lq,
+                                              int32_t Lk, int32_t dtype);
+ARL2_API arl2_status arl2_softmax_attention(const void *q, const void *kc, const void *vc, int32_t B,
+                                   int32_t H, int32_t d, int32_t Lq, int32_t Lk, int32_t dtype,
+                                   void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a status code (never NULL). */
+ARL2_API const char *arl2_status_string(int32_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+ARL2_API const char *arl2_last_error(void);
+
+/* ARL2_VERSION of the loaded library. */
+ARL2_API int32_t arl2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ARL2_H */

@@ -46,19 +46,22 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Returns the 16-bit patterns as uint16. NaN inputs stay NaN (quiet bit set).
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    rounded = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint32)
+    u = x.view(np.uint32)
     nan = np.isnan(x)
+    # For every non-NaN pattern the sum stays below 2**32.
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    out = (r >> np.uint32(16)).astype(np.uint16)
     if nan.any():
-        rounded = np.where(nan, ((u >> np.uint64(16)).astype(np.uint32)) | np.uint32(0x40), rounded)
-    return rounded.astype(np.uint16)
+        out = np.where(nan, ((u >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16), out)
+    return out
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Widen bfloat16 patterns (uint16) to the float32 values they encode (exact)."""
     b = np.ascontiguousarray(bits, dtype=np.uint16)
-    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    out = np.empty(b.shape, dtype=np.uint32)
+    np.left_shift(b, 16, out=out, dtype=np.uint32)
+    return out.view(np.float32)
 
 
 def round_f32_to_bf16_values(x: np.ndarray) -> np.ndarray:
@@ -195,3 +198,61 @@ def random_pass(B: int, H: int, d: int, L: int, dtype: str, seed: int,
     pi = next(iter_passes(w))
     pi.update = update
     return pi
+
+
+# ------------------------------------------------------- device-side drawing
+@dataclasses.dataclass
+class DevicePass:
+    """One pass drawn on a torch device: q, k, v [B][L][H][d] in the io dtype,
+    alpha [B][H] and beta [B][L][H] float32."""
+
+    frame: int
+    index: int
+    update: bool
+    q: "object"
+    k: "object"
+    v: "object"
+    alpha: "object"
+    beta: "object"
+
+
+def torch_dtype(dtype: str):
+    import torch
+    return torch.bfloat16 if dtype == BF16 else torch.float32
+
+
+def iter_passes_device(w: Workload, device, frames: Optional[int] = None) -> Iterator[DevicePass]:
+    """The same recipe as ``iter_passes``, drawn with torch's seeded generator
+    on ``device`` (Philox on a GPU), for streams too long to draw on the host.
+
+    Per stream b (generator seeded with 1_000_003 * (seed + b) + 13) the draw
+    order is: for each frame, alpha [H] and beta [L][H] of the frame, then for
+    each pass q, k, v ([L][H][d] each, float32, then rounded to the io dtype
+    with round-to-nearest-even). Consumers that need host copies (the oracle)
+    copy these exact tensors back, so both sides read the same bytes.
+    """
+    import torch
+    nf = w.frames if frames is None else frames
+    gens = []
+    for b in range(w.B):
+        g = torch.Generator(device=device)
+        g.manual_seed(1_000_003 * (w.seed + b) + _TAG_STREAM)
+        gens.append(g)
+    io = torch_dtype(w.dtype)
+    shape = (w.L, w.H, w.d)
+    for f in range(nf):
+        alpha = torch.empty((w.B, w.H), dtype=torch.float32, device=device)
+        beta = torch.empty((w.B, w.L, w.H), dtype=torch.float32, device=device)
+        for b, g in enumerate(gens):
+            alpha[b] = torch.sigmoid(2.0 + 0.5 * torch.randn(w.H, generator=g, device=device))
+            beta[b] = torch.sigmoid(torch.randn((w.L, w.H), generator=g, device=device))
+        if w.beta_scale != 1.0:
+            beta *= w.beta_scale
+        for p in range(w.passes_per_frame):
+            t = []
+            for _name in ("q", "k", "v"):
+                x = torch.empty((w.B,) + shape, dtype=io, device=device)
+                for b, g in enumerate(gens):
+                    x[b] = torch.randn(shape, generator=g, device=device).to(io)
+                t.append(x)
+            yield DevicePass(f, p, p == w.passes_per_frame - 1, t[0], t[1], t[2], alpha, beta)

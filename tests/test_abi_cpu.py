@@ -1,0 +1,178 @@
+"""The C ABI without a GPU: the library loads, exports exactly what
+include/arl2.h declares, and rejects bad arguments before touching HIP.
+
+No call here reaches a kernel: every case fails validation, which runs
+before anything is enqueued. Fake device addresses are plain integers that
+are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "arl2.h")
+
+
+
+@pytest.fixture(scope="module")
+def B():
+    from hybrid_softmax_gated_amd import binding
+    return binding
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"ARL2_API\s+[\w\s\*]*?\b(arl2_\w+)\s*\(", text))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    assert {"arl2_state_init", "arl2_state_reset", "arl2_frame_forward",
+            "arl2_workspace_bytes"} <= names
+    assert len(names) == 9
+
+
+def test_library_exports_every_declared_symbol(B):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert _declared() <= exported
+    # nothing else with the public prefix leaks out
+    assert {e for e in exported if e.startswith("arl2_")} == _declared()
+    assert set(B.EXPORTED) == _declared()
+
+
+def test_version_and_status_strings(B):
+    assert B.arl2_version() == 1
+    assert B.arl2_status_string(0) == "ok"
+    assert B.arl2_status_string(1) == "invalid argument"
+    assert B.arl2_status_string(2) == "unsupported"
+    assert B.arl2_status_string(3) == "HIP runtime error"
+    assert B.arl2_status_string(99) == "unknown status"
+
+
+def test_state_struct_layout_matches_c(B):
+    assert ctypes.sizeof(B.arl2_state) == 6 * 4 + 3 * 8
+    assert B.arl2_state.S.offset == 24 and B.arl2_state.ws_bytes.offset == 40
+
+
+def test_workspace_bytes(B):
+    n = B.arl2_workspace_bytes(1, 12, 128, 1560, B.ARL2_BF16)
+    assert n > 0 and n % 256 == 0
+    # independent of the number of frames by construction; grows with L
+    assert B.arl2_workspace_bytes(1, 12, 128, 3600, B.ARL2_BF16) > n
+    assert B.arl2_workspace_bytes(1, 1, 16, 64, B.ARL2_F32) > 0
+    for bad in [(0, 12, 128, 1560, 0), (1, 0, 128, 1560, 0), (1, 12, 64, 1560, 0),
+                (1, 12, 128, 0, 0), (1, 12, 128, 1560, 7), (1, 12, 128, (1 << 20) + 1, 0)]:
+        assert B.arl2_workspace_bytes(*bad) == 0
+
+
+FAKE_S = 0x7F0000000000
+FAKE_WS = 0x7F1000000000
+
+
+def _code(fn, *a):
+    from hybrid_softmax_gated_amd.binding import ARL2Error
+    with pytest.raises(ARL2Error) as ei:
+        fn(*a)
+    return ei.value.status, str(ei.value)
+
+
+def test_state_init_validation(B):
+    st = B.arl2_state()
+    ws = B.arl2_workspace_bytes(1, 2, 128, 100, B.ARL2_BF16)
+    assert _code(B.arl2_state_init, st, 1, 2, 64, 100, 0, FAKE_S, FAKE_WS, ws)[0] == B.ARL2_ERR_UNSUPPORTED
+    assert _code(B.arl2_state_init, st, 0, 2, 128, 100, 0, FAKE_S, FAKE_WS, ws)[0] == B.ARL2_ERR_INVALID_ARG
+    assert _code(B.arl2_state_init, st, 1, 2, 128, 100, 5, FAKE_S, FAKE_WS, ws)[0] == B.ARL2_ERR_INVALID_ARG
+    assert _code(B.arl2_state_init, st, 1, 2, 128, 100, 0, None, FAKE_WS, ws)[0] == B.ARL2_ERR_INVALID_ARG
+    assert _code(B.arl2_state_init, st, 1, 2, 128, 100, 0, FAKE_S + 4, FAKE_WS, ws)[0] == B.ARL2_ERR_INVALID_ARG
+    code, msg = _code(B.arl2_state_init, st, 1, 2, 128, 100, 0, FAKE_S, FAKE_WS, ws - 256)
+    assert code == B.ARL2_ERR_INVALID_ARG and "workspace" in msg
+    assert _code(B.arl2_state_init, st, 1, 2, 128, 100, 0, FAKE_S, FAKE_WS + 16, ws)[0] == B.ARL2_ERR_INVALID_ARG
+    assert _code(B.arl2_state_init, st, 1, 2, 128, 100, 0, FAKE_S, None, ws)[0] == B.ARL2_ERR_INVALID_ARG
+    # state overlapping its workspace
+    assert _code(B.arl2_state_init, st, 1, 2, 128, 100, 0, FAKE_WS, FAKE_WS, ws)[0] == B.ARL2_ERR_INVALID_ARG
+    assert st.magic == 0, "a failed init must leave the descriptor untouched"
+
+
+def _fake_state(B, Bn=1, H=2, d=128, L=100, dtype=0):
+    """A descriptor that passes the state checks, pointing at fake memory."""
+    st = B.arl2_state()
+    st.B, st.H, st.d, st.L, st.dtype = Bn, H, d, L, dtype
+    st.magic = 0x41524C32
+    st.S = FAKE_S
+    st.ws = FAKE_WS
+    st.ws_bytes = B.arl2_workspace_bytes(Bn, H, d, L, dtype)
+    return st
+
+
+Q, K, V, W, OUT, AL, BE = (0x7E0000000000 + i * 0x1000000000 for i in range(7))
+
+
+def test_frame_forward_validation(B):
+    st = _fake_state(B)
+    E = B.ARL2_ERR_INVALID_ARG
+    assert _code(B.arl2_frame_forward, Q, K, V, W, B.arl2_state(), AL, BE, OUT, 1)[0] == E
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL, BE, OUT, 2)[0] == E
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL, BE, OUT, -1)[0] == E
+    assert _code(B.arl2_frame_forward, None, K, V, W, st, AL, BE, OUT, 0)[0] == E
+    assert _code(B.arl2_frame_forward, Q, K, V, None, st, AL, BE, OUT, 0)[0] == E
+    assert _code(B.arl2_frame_forward, Q + 2, K, V, W, st, AL, BE, OUT, 0)[0] == E
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st, None, BE, OUT, 1)[0] == E
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL, None, OUT, 1)[0] == E
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL + 2, BE, OUT, 1)[0] == E
+    # out aliasing an input, the state or the workspace
+    assert "overlaps" in _code(B.arl2_frame_forward, Q, K, V, W, st, AL, BE, Q + 256, 0)[1]
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL, BE, FAKE_S, 0)[0] == E
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL, BE, FAKE_WS + 1024, 0)[0] == E
+    # an input overlapping the state (it would be overwritten by the update)
+    assert _code(B.arl2_frame_forward, FAKE_S, K, V, W, st, AL, BE, OUT, 1)[0] == E
+    # beta overlapping the state
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL, FAKE_S, OUT, 1)[0] == E
+    # a workspace that is too small for the state's shape
+    st.ws_bytes -= 256
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL, BE, OUT, 0)[0] == E
+    st2 = _fake_state(B, d=32)
+    assert _code(B.arl2_frame_forward, Q, K, V, W, st2, AL, BE, OUT, 0)[0] == B.ARL2_ERR_UNSUPPORTED
+    assert B.arl2_last_error()  # the detail of the last failure is kept
+
+
+def test_state_reset_validation(B):
+    E = B.ARL2_ERR_INVALID_ARG
+    assert _code(B.arl2_state_reset, B.arl2_state(), None)[0] == E
+    st = _fake_state(B)
+    assert _code(B.arl2_state_reset, st, FAKE_S + 64)[0] == E   # S0 overlaps S
+    assert _code(B.arl2_state_reset, st, FAKE_S + (1 << 30) + 2)[0] == E  # misaligned
+
+
+def test_softmax_attention_validation(B):
+    E = B.ARL2_ERR_INVALID_ARG
+    nb = B.arl2_softmax_attention_workspace_bytes(1, 12, 128, 1560, 4680, 0)
+    assert nb > 0
+    assert B.arl2_softmax_attention_workspace_bytes(1, 12, 128, 1560, 0, 0) == 0
+    assert _code(B.arl2_softmax_attention, Q, K, V, 1, 12, 128, 1560, 4680, 0, OUT, FAKE_WS, nb - 1)[0] == E
+    assert _code(B.arl2_softmax_attention, Q, K, V, 1, 12, 128, 1560, 4680, 0, OUT, None, nb)[0] == E
+    assert _code(B.arl2_softmax_attention, Q, K, V, 1, 12, 128, 1560, 4680, 0, Q, FAKE_WS, nb)[0] == E
+    assert _code(B.arl2_softmax_attention, Q, K, V, 1, 12, 48, 1560, 4680, 0, OUT, FAKE_WS, nb)[0] == B.ARL2_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_to_load_without_the_library(repo_root):
+    # Importing the package does not load the library; loading the binding
+    # from a path with no library raises ImportError (no silent fallback).
+    code = "\n".join([
+        "import sys",
+        "sys.path.insert(0, %r)" % repo_root,
+        "import hybrid_softmax_gated_amd as p",
+        "assert 'hybrid_softmax_gated_amd.binding' not in sys.modules",
+        "import hybrid_softmax_gated_amd.binding as b",
+        "b.LIB_PATH = '/nonexistent/libarl2.so'",
+        "try:",
+        "    b._load()",
+        "except ImportError:",
+        "    print('raised')",
+    ])
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True)
+    assert "raised" in r.stdout, r.stderr

@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Throughput of one ARL2 hybrid attention layer on one MI355X.
+
+One step = one latent frame through one layer: every pass of the frame (the
+query-only denoising pass(es), then the clean pass that updates the state),
+i.e. every step of the hot path: intra-frame softmax attention, feature maps
+with L2 norms, the frame-level read of the state, the combine, and the gated
+delta update. Default workload: the Wan2.1-1.3B 480p frame step (B=1, 12
+heads of 128, L=1560 tokens, 1 query-only + 1 clean pass per frame).
+
+Inputs are synthetic and seeded (q, k, v ~ N(0,1) in bf16, W = I + N(0,0.01),
+alpha = sigmoid(N(2,0.5)), beta = sigmoid(N(0,1)) / L so that the state stays
+finite over thousands of back-to-back frames; the work does not depend on the
+values). A set of distinct frames is drawn on the GPU before timing and
+cycled; everything is resident in HBM when the timed region starts.
+
+Prints one JSON line (the driver's contract) with, besides frames/s:
+  roofline      the dominant kernel (intra-frame attention) against the bf16
+                dense MFMA peak, from its average launch duration measured
+                with HIP events on its launch stream (arl2_profile_*);
+  cpu_baseline  the float64 oracle on this host's cores, on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-layer frames/sec + TFLOP/s (% MFMA peak), L=1560 d=128 12 heads"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4 SIMD x 1024 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+NUM_DISTINCT_FRAMES = 8
+
+
+def flops(B, H, d, L):
+    """Algorithmic MFMA-eligible flops: intra attention (QK^T and PV),
+    phi_q + read, and the delta update (phi_k, phi_v, K'S, K'^T R)."""
+    fa = 4.0 * B * H * L * L * d
+    fb = 4.0 * B * H * L * d * d
+    fc = 8.0 * B * H * L * d * d
+    return fa, fb, fc
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "hybrid_softmax_gated_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != digest:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(frames_host, W, w, budget_s=12.0, max_frames=24):
+    """Time the float64 oracle on host copies of the same frames."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    S = np.zeros((w.B, w.H, w.d, w.d))
+    Wf = W.astype(np.float64)
+    done = 0
+    t0 = time.perf_counter()
+    while done < max_frames and (time.perf_counter() - t0) < budget_s:
+        for p in frames_host[done % len(frames_host)]:
+            O.frame_forward(p["q"], p["k"], p["v"], Wf, S, p["alpha"], p["beta"], int(p["update"]))
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} full frames ({w.noisy_passes} query-only + 1 clean pass each) of "
+                      f"{w.name}, all {w.H} heads, float64 NumPy/OpenBLAS, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="frame_step_480p",
+                    choices=["frame_step_480p", "stream21_480p", "batched720p"])
+    ap.add_argument("--profile-steps", type=int, default=300)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads and streams shard with no exchange; see the sharding note in the design)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth_inputs as SI
+    from hybrid_softmax_gated_amd import binding as Bd
+    from hybrid_softmax_gated_amd.layer import ARL2Layer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = SI.companion(SI.WORKLOADS[args.workload])
+    B, H, d, L = w.B, w.H, w.d, w.L
+
+    # ---- inputs, resident in HBM before timing
+    W = SI.make_weights(w)
+    Wd = torch.from_numpy(W).to(dev).to(torch.bfloat16)
+    frames = []
+    gen = SI.iter_passes_device(w, dev, frames=NUM_DISTINCT_FRAMES)
+    cur = []
+    for p in gen:
+        cur.append(p)
+        if p.update:
+            frames.append(cur)
+            cur = []
+    layer = ARL2Layer(B, H, d, L, Bd.ARL2_BF16)
+    out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        for p in frames[i % len(frames)]:
+            layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region (single process: the barrier is the synchronize)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    fps = args.steps / wall
+    assert torch.isfinite(layer.S).all(), "state went non-finite during the benchmark"
+
+    # ---- per-kernel durations with HIP events on the launch stream
+    Bd.arl2_profile_reset()
+    Bd.arl2_profile_enable(True)
+    for i in range(args.profile_steps):
+        step(i)
+    torch.cuda.synchronize()
+    rep = Bd.arl2_profile_report()
+    Bd.arl2_profile_enable(False)
+    kern_us = {k: 1000.0 * ms / n for k, (n, ms) in rep.items() if n}
+
+    fa, fb, fc = flops(B, H, d, L)
+    passes = w.passes_per_frame
+    frame_flops = passes * (fa + fb) + fc
+    tflops = frame_flops * fps / 1e12
+    att_s = kern_us["attn_partial"] * 1e-6
+    att_tflops = fa / att_s / 1e12
+    digest = source_digest("attn.hip", "arl2_device.h", "mfma_stage.h")
+    roofline = {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic("attn_partial", args.workload, digest),
+                "kernel": "attn_partial",
+                "per_launch": f"4*B*H*L^2*d = {fa / 1e9:.3f} GFLOP (one pass, B={B} H={H} L={L} d={d})",
+                "avg_launch_us": round(kern_us["attn_partial"], 2)}
+
+    res = {
+        "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1000.0 * wall / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "d": d, "L": L,
+                   "passes_per_frame": f"{w.noisy_passes} query-only + 1 clean",
+                   "distinct_frames_cycled": NUM_DISTINCT_FRAMES},
+        "tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "gflop_per_frame": round(frame_flops / 1e9, 3),
+        "event_ms_per_step": round(ev_ms / args.steps, 5),
+        "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        host = []
+        for fr in frames[:2]:
+            host.append([{"q": p.q.float().cpu().numpy(), "k": p.k.float().cpu().numpy(),
+                          "v": p.v.float().cpu().numpy(), "alpha": p.alpha.cpu().numpy(),
+                          "beta": p.beta.cpu().numpy(), "update": p.update} for p in fr])
+        res["cpu_baseline"] = cpu_baseline(host, W, w)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

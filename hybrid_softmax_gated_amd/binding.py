@@ -24,7 +24,10 @@ ARL2_ERR_HIP = 3
 ARL2_BF16 = 0
 ARL2_F32 = 1
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarl2.so")
+# The in-tree library; ARL2_LIBRARY may name another build of the same ABI
+# (for comparing kernel variants).
+LIB_PATH = os.environ.get("ARL2_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libarl2.so")
 
 
 class arl2_state(ctypes.Structure):
@@ -65,6 +68,9 @@ def _load() -> ctypes.CDLL:
         "arl2_frame_forward": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, P, P, I, P]),
         "arl2_softmax_attention_workspace_bytes": (Z, [I, I, I, I, I, I]),
         "arl2_softmax_attention": (I, [P, P, P, I, I, I, I, I, I, P, P, Z, P]),
+        "arl2_profile_enable": (I, [I]),
+        "arl2_profile_report": (I, [ctypes.c_char_p, Z]),
+        "arl2_profile_reset": (None, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -77,7 +83,8 @@ _lib = _load()
 
 EXPORTED = ("arl2_version", "arl2_status_string", "arl2_last_error", "arl2_workspace_bytes",
             "arl2_state_init", "arl2_state_reset", "arl2_frame_forward",
-            "arl2_softmax_attention_workspace_bytes", "arl2_softmax_attention")
+            "arl2_softmax_attention_workspace_bytes", "arl2_softmax_attention",
+            "arl2_profile_enable", "arl2_profile_report", "arl2_profile_reset")
 
 
 def _ptr(x):
@@ -147,3 +154,22 @@ def arl2_softmax_attention(q, kc, vc, B: int, H: int, d: int, Lq: int, Lk: int, 
                            ws, ws_bytes: int, stream=None) -> None:
     _check(_lib.arl2_softmax_attention(_ptr(q), _ptr(kc), _ptr(vc), B, H, d, Lq, Lk, dtype,
                                        _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def arl2_profile_enable(on: bool) -> None:
+    _check(_lib.arl2_profile_enable(1 if on else 0))
+
+
+def arl2_profile_reset() -> None:
+    _lib.arl2_profile_reset()
+
+
+def arl2_profile_report() -> dict:
+    """{kernel name: (launches, total_ms)} for the launches timed so far."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(_lib.arl2_profile_report(buf, len(buf)))
+    res = {}
+    for line in buf.value.decode().splitlines():
+        name, n, ms = line.split()
+        res[name] = (int(n), float(ms))
+    return res

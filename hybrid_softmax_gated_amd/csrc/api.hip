@@ -18,6 +18,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <string>
+#include <vector>
+
 #include "arl2_kernels.h"
 
 namespace {
@@ -129,6 +133,82 @@ AttnOnlyPlan plan_attn_only(int64_t B, int64_t H, int64_t d, int64_t Lq, int64_t
   return p;
 }
 
+// ------------------------------------------------------------ kernel timing
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  struct Rec {
+    size_t kernel;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> spare;
+  std::vector<std::string> names;
+  std::vector<int64_t> launches;
+  std::vector<double> total_ms;
+
+  hipError_t event(hipEvent_t *e) {
+    if (!spare.empty()) {
+      *e = spare.back();
+      spare.pop_back();
+      return hipSuccess;
+    }
+    return hipEventCreate(e);
+  }
+  size_t id(const char *name) {
+    for (size_t i = 0; i < names.size(); ++i)
+      if (names[i] == name) return i;
+    names.emplace_back(name);
+    launches.push_back(0);
+    total_ms.push_back(0.0);
+    return names.size() - 1;
+  }
+  // Wait for every recorded pair and fold it into the totals.
+  hipError_t drain() {
+    hipError_t err = hipSuccess;
+    for (const Rec &r : pending) {
+      float ms = 0.f;
+      hipError_t e = hipEventSynchronize(r.b);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+      if (e == hipSuccess) {
+        launches[r.kernel] += 1;
+        total_ms[r.kernel] += ms;
+      } else if (err == hipSuccess) {
+        err = e;
+      }
+      spare.push_back(r.a);
+      spare.push_back(r.b);
+    }
+    pending.clear();
+    return err;
+  }
+};
+
+Profiler &profiler() {
+  static Profiler p;
+  return p;
+}
+
+// Launch through `fn`, bracketed by timing events when profiling is on.
+template <class F>
+hipError_t timed(const char *name, hipStream_t s, F fn) {
+  Profiler &p = profiler();
+  std::unique_lock<std::mutex> lk(p.mu);
+  if (!p.on) {
+    lk.unlock();
+    return fn();
+  }
+  hipEvent_t a, b;
+  hipError_t e = p.event(&a);
+  if (e != hipSuccess) return e;
+  if ((e = p.event(&b)) != hipSuccess) return e;
+  if ((e = hipEventRecord(a, s)) != hipSuccess) return e;
+  if ((e = fn()) != hipSuccess) return e;
+  if ((e = hipEventRecord(b, s)) != hipSuccess) return e;
+  p.pending.push_back({p.id(name), a, b});
+  return hipSuccess;
+}
+
 arl2_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return ARL2_OK;
   return fail(ARL2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -177,7 +257,7 @@ arl2_status arl2_state_init(arl2_state *st, int32_t B, int32_t H, int32_t d, int
   if (ws_dev && overlap(range(S_dev, s_bytes), range(ws_dev, ws_bytes)))
     return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: S and workspace overlap");
   arl2_status hs = hip_status(
-      arl2::launch_fill_state(S_dev, nullptr, (int64_t)B * H * d * d, (hipStream_t)stream),
+      timed("fill_state", (hipStream_t)stream, [&] { return arl2::launch_fill_state(S_dev, nullptr, (int64_t)B * H * d * d, (hipStream_t)stream); }),
       "arl2_state_init");
   if (hs != ARL2_OK) return hs;
   st->B = B;
@@ -213,7 +293,7 @@ arl2_status arl2_state_reset(arl2_state *st, const float *S0_dev, void *stream) 
     if (overlap(range(S0_dev, n * sizeof(float)), range(st->S, n * sizeof(float))))
       return fail(ARL2_ERR_INVALID_ARG, "arl2_state_reset: S0 overlaps S");
   }
-  arl2_status hs = hip_status(arl2::launch_fill_state(st->S, S0_dev, n, (hipStream_t)stream),
+  arl2_status hs = hip_status(timed("fill_state", (hipStream_t)stream, [&] { return arl2::launch_fill_state(st->S, S0_dev, n, (hipStream_t)stream); }),
                               "arl2_state_reset");
   if (hs != ARL2_OK) return hs;
   return ok();
@@ -273,32 +353,43 @@ arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, cons
   const void *Wk = wbase + (size_t)H * d * d * es;
   const void *Wv = wbase + (size_t)2 * H * d * d * es;
 
+  const int iB = (int)B, iH = (int)H, iL = (int)L, id = (int)d, dt = st->dtype;
+  float *S = st->S;
   hipError_t e;
   if (fp.mfma) {
-    arl2::AttnArgs aa{q, k, v, (int)B, (int)H, (int)L, (int)L, fp.ap, ws_o, ws_ml};
-    if ((e = arl2::launch_attn_partial_bf16(aa, s)) != hipSuccess) return hip_status(e, fn);
-    arl2::CombineArgs ca{q, Wq, st->S, (int)B, (int)H, (int)L, fp.ap, ws_o, ws_ml, out, true};
-    if ((e = arl2::launch_inter_combine_bf16(ca, s)) != hipSuccess) return hip_status(e, fn);
+    const arl2::AttnArgs aa{q, k, v, iB, iH, iL, iL, fp.ap, ws_o, ws_ml};
+    const arl2::CombineArgs ca{q, Wq, S, iB, iH, iL, fp.ap, ws_o, ws_ml, out, true};
+    if ((e = timed("attn_partial", s, [&] { return arl2::launch_attn_partial_bf16(aa, s); })))
+      return hip_status(e, fn);
+    if ((e = timed("inter_combine", s, [&] { return arl2::launch_inter_combine_bf16(ca, s); })))
+      return hip_status(e, fn);
     if (update_flag) {
-      arl2::DeltaArgs da{k, v, Wk, Wv, st->S, beta, (int)B, (int)H, (int)L, fp.nchunk, ws_ds};
-      if ((e = arl2::launch_delta_partial_bf16(da, s)) != hipSuccess) return hip_status(e, fn);
+      const arl2::DeltaArgs da{k, v, Wk, Wv, S, beta, iB, iH, iL, fp.nchunk, ws_ds};
+      if ((e = timed("delta_partial", s, [&] { return arl2::launch_delta_partial_bf16(da, s); })))
+        return hip_status(e, fn);
     }
   } else {
-    if ((e = arl2::launch_generic_attention(st->dtype, (int)d, q, k, v, (int)B, (int)H, (int)L,
-                                            (int)L, ws_o, s)) != hipSuccess)
+    if ((e = timed("generic_attention", s, [&] {
+           return arl2::launch_generic_attention(dt, id, q, k, v, iB, iH, iL, iL, ws_o, s);
+         })))
       return hip_status(e, fn);
-    if ((e = arl2::launch_generic_inter_combine(st->dtype, (int)d, q, Wq, st->S, ws_o, (int)B,
-                                                (int)H, (int)L, out, true, s)) != hipSuccess)
+    if ((e = timed("generic_inter_combine", s, [&] {
+           return arl2::launch_generic_inter_combine(dt, id, q, Wq, S, ws_o, iB, iH, iL, out, true,
+                                                     s);
+         })))
       return hip_status(e, fn);
     if (update_flag) {
-      if ((e = arl2::launch_generic_delta_partial(st->dtype, (int)d, k, v, Wk, Wv, st->S, beta,
-                                                  (int)B, (int)H, (int)L, ws_ds, s)) != hipSuccess)
+      if ((e = timed("generic_delta_partial", s, [&] {
+             return arl2::launch_generic_delta_partial(dt, id, k, v, Wk, Wv, S, beta, iB, iH, iL,
+                                                       ws_ds, s);
+           })))
         return hip_status(e, fn);
     }
   }
   if (update_flag) {
-    if ((e = arl2::launch_delta_apply(st->S, alpha, ws_ds, (int)B, (int)H, (int)d, fp.nchunk,
-                                      s)) != hipSuccess)
+    if ((e = timed("delta_apply", s, [&] {
+           return arl2::launch_delta_apply(S, alpha, ws_ds, iB, iH, id, fp.nchunk, s);
+         })))
       return hip_status(e, fn);
   }
   return ok();
@@ -349,18 +440,57 @@ arl2_status arl2_softmax_attention(const void *q, const void *kc, const void *vc
   float *ws_ml = (float *)((char *)ws + ap.off_ml);
   hipError_t e;
   if (ap.mfma) {
-    arl2::AttnArgs aa{q, kc, vc, B, H, Lq, Lk, ap.ap, ws_o, ws_ml};
-    if ((e = arl2::launch_attn_partial_bf16(aa, s)) != hipSuccess) return hip_status(e, fn);
-    arl2::CombineArgs ca{q, nullptr, nullptr, B, H, Lq, ap.ap, ws_o, ws_ml, out, false};
-    if ((e = arl2::launch_inter_combine_bf16(ca, s)) != hipSuccess) return hip_status(e, fn);
-  } else {
-    if ((e = arl2::launch_generic_attention(dtype, d, q, kc, vc, B, H, Lq, Lk, ws_o, s)) !=
-        hipSuccess)
+    const arl2::AttnArgs aa{q, kc, vc, B, H, Lq, Lk, ap.ap, ws_o, ws_ml};
+    const arl2::CombineArgs ca{q, nullptr, nullptr, B, H, Lq, ap.ap, ws_o, ws_ml, out, false};
+    if ((e = timed("attn_partial", s, [&] { return arl2::launch_attn_partial_bf16(aa, s); })))
       return hip_status(e, fn);
-    if ((e = arl2::launch_generic_inter_combine(dtype, d, q, nullptr, nullptr, ws_o, B, H, Lq,
-                                                out, false, s)) != hipSuccess)
+    if ((e = timed("attn_merge", s, [&] { return arl2::launch_inter_combine_bf16(ca, s); })))
+      return hip_status(e, fn);
+  } else {
+    if ((e = timed("generic_attention", s, [&] {
+           return arl2::launch_generic_attention(dtype, d, q, kc, vc, B, H, Lq, Lk, ws_o, s);
+         })))
+      return hip_status(e, fn);
+    if ((e = timed("generic_attn_merge", s, [&] {
+           return arl2::launch_generic_inter_combine(dtype, d, q, nullptr, nullptr, ws_o, B, H, Lq,
+                                                     out, false, s);
+         })))
       return hip_status(e, fn);
   }
+  return ok();
+}
+
+arl2_status arl2_profile_enable(int32_t on) {
+  Profiler &p = profiler();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.on = on != 0;
+  return ok();
+}
+
+void arl2_profile_reset(void) {
+  Profiler &p = profiler();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.drain();
+  for (size_t i = 0; i < p.names.size(); ++i) {
+    p.launches[i] = 0;
+    p.total_ms[i] = 0.0;
+  }
+}
+
+arl2_status arl2_profile_report(char *buf, size_t len) {
+  if (!buf || len == 0) return fail(ARL2_ERR_INVALID_ARG, "arl2_profile_report: no buffer");
+  Profiler &p = profiler();
+  std::lock_guard<std::mutex> lk(p.mu);
+  const hipError_t e = p.drain();
+  std::string txt;
+  char line[160];
+  for (size_t i = 0; i < p.names.size(); ++i) {
+    snprintf(line, sizeof(line), "%s %lld %.6f\n", p.names[i].c_str(), (long long)p.launches[i],
+             p.total_ms[i]);
+    txt += line;
+  }
+  snprintf(buf, len, "%s", txt.c_str());
+  if (e != hipSuccess) return hip_status(e, "arl2_profile_report");
   return ok();
 }
 

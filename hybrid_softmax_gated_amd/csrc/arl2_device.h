@@ -57,6 +57,37 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// LDS tile of 16-bit elements with 256-byte rows (128 bf16), stored as 16
+// units of 16 bytes per row; unit u of row r sits at position u ^ tile_swz(r)
+// so that both access patterns below are free of bank conflicts:
+//  * 16 lanes reading the same unit of 16 consecutive rows (b128 reads);
+//  * transpose reads: 4 consecutive rows x 2 adjacent units per 16 lanes.
+__device__ __host__ __forceinline__ constexpr int tile_swz(int r) {
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+__device__ __forceinline__ int tile_off(int row, int unit) {
+  return row * 256 + ((unit ^ tile_swz(row & 15)) << 4);
+}
+
+// Transposed LDS read (gfx950): within each group of 16 lanes, lane i
+// receives element i%4 of the 8-byte words addressed by lanes i/4, 4+i/4,
+// 8+i/4 and 12+i/4 of its group. If lane j of a group addresses row
+// r0 + j/4, columns c0 + 4*(j%4) .. +3 of a row-major 16-bit matrix, lane i
+// receives rows r0 .. r0+3 of column c0 + i.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void *lds_byte_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(lds_byte_addr));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane i's 16 bytes land at
+// lds_base + 16 * i (lds_base must be uniform across the wavefront).
+__device__ __forceinline__ void global_to_lds16(const void *gsrc, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t *)lds_base, 16, 0, 0);
+}
+
 // Split an fp32 value into bf16 high and low parts, x ~= hi + lo (the
 // three-product bf16 scheme of Henry, Tang and Heinecke, ARITH 2019).
 __device__ __forceinline__ void split_bf16(float x, bf16 &hi, bf16 &lo) {

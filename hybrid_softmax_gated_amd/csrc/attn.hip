@@ -28,7 +28,6 @@
 //    written per key range; the epilogue merges the ranges.
 #include "arl2_device.h"
 #include "arl2_kernels.h"
-#include "mfma_stage.h"
 
 #include <math.h>
 
@@ -37,29 +36,84 @@ namespace {
 
 constexpr int D = 128;
 constexpr int KB = kKeyTile;  // 64 keys per LDS tile
-constexpr int KS_LD = D + 8;  // K tile row stride (bf16): 272 B, conflict-free b128 reads
-constexpr int VT_LD = KB + 8; // V^T tile row stride (bf16): 144 B
 
 struct AttnKParams {
   const bf16 *q, *k, *v;
   int H, Lq, Lk, nsplit, kps, nqblk;
+  int nitems, per_xcd;  // work items and items per XCD (see item_of)
   float *ws_o, *ws_ml;
   float scale;  // log2(e) / sqrt(d)
 };
 
-__global__ __launch_bounds__(256) void attn_partial_kernel(AttnKParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KB * KS_LD];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * VT_LD];
+// Work items are (stream, head, split, query block) with the query block
+// fastest, so that consecutive items share one key range of one head.
+// Workgroups are dealt to the 8 XCDs round-robin by linear id; item_of gives
+// every XCD a contiguous run of items, so the K/V rows a run touches stay in
+// that XCD's L2.
+__device__ __forceinline__ int item_of(int bid, int per_xcd) {
+  return (bid & 7) * per_xcd + (bid >> 3);
+}
+
+// Issue the direct global->LDS copy of one 64-key tile (64 rows of 256 B,
+// swizzled): 16 chunks of 4 rows, 4 per wavefront. Rows past the key range
+// re-read the last valid row (finite values; their scores are masked).
+__device__ __forceinline__ void issue_tile(const bf16 *__restrict__ base, int64_t tok, int t0,
+                                           int kend, bf16 *tile, int wave, int lane) {
+  const int r4 = lane >> 4, pos = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int cc = 4 * wave + i;
+    const int row = 4 * cc + r4;
+    const int key = min(t0 + row, kend - 1);
+    const int unit = pos ^ tile_swz(row & 15);
+    global_to_lds16(base + key * tok + 8 * unit, tile + cc * 512);
+  }
+}
+
+// Register-staged copy of one 64-key tile into the same swizzled layout:
+// thread t owns rows t/16 + 16i (i = 0..3), unit t%16.
+__device__ __forceinline__ void load_tile_regs(const bf16 *__restrict__ base, int64_t tok, int t0,
+                                               int kend, int tid, bf16x8 (&r)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = min(t0 + (tid >> 4) + 16 * i, kend - 1);
+    r[i] = *(const bf16x8 *)(base + key * tok + 8 * (tid & 15));
+  }
+}
+__device__ __forceinline__ void store_tile_regs(char *tile, int tid, const bf16x8 (&r)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *(bf16x8 *)(tile + tile_off((tid >> 4) + 16 * i, tid & 15)) = r[i];
+}
+
+__global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
+  __shared__ __attribute__((aligned(1024))) bf16 Kt0[KB * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Kt1[KB * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vt0[KB * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vt1[KB * D];
+
+  const int item = item_of(blockIdx.x, p.per_xcd);
+  if (item >= p.nitems) return;
+  const int qblk = item % p.nqblk;
+  int rest = item / p.nqblk;
+  const int split = rest % p.nsplit;
+  rest /= p.nsplit;
+  const int h = rest % p.H, b = rest / p.H;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-  const int split = blockIdx.x % p.nsplit;
-  const int qblk = blockIdx.x / p.nsplit;
-  const int h = blockIdx.y, b = blockIdx.z;
   const int64_t tok = (int64_t)p.H * D;
   const bf16 *qbase = p.q + ((int64_t)b * p.Lq * p.H + h) * D;
   const bf16 *kbase = p.k + ((int64_t)b * p.Lk * p.H + h) * D;
   const bf16 *vbase = p.v + ((int64_t)b * p.Lk * p.H + h) * D;
+  const int kbeg = split * p.kps;
+  const int kend = min(p.Lk, kbeg + p.kps);
+
+  bf16x8 kreg[4], vreg[4];
+  load_tile_regs(kbase, tok, kbeg, kend, tid, kreg);
+  load_tile_regs(vbase, tok, kbeg, kend, tid, vreg);
+  store_tile_regs((char *)Kt0, tid, kreg);
+  store_tile_regs((char *)Vt0, tid, vreg);
 
   // The wavefront's 32 queries as B operands: lane l holds query l%32,
   // head-dim elements 16c + 8*(l/32) .. +7.
@@ -79,45 +133,36 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnKParams p) {
   for (int bb = 0; bb < 4; ++bb) o[bb] = zero16();
   float m = -INFINITY, lsum = 0.f;
 
-  const int kbeg = split * p.kps;
-  const int kend = min(p.Lk, kbeg + p.kps);
-
-  // Tile staging: K as 4 rows x 16 B per thread (coalesced rows), V as
-  // 4 consecutive keys x 8 head-dim values per thread (for the transpose).
-  const int kd = tid & 15, kr0 = tid >> 4;
-  const int vg = tid & 15, vd = tid >> 4;
-  const int vpos = 4 * swap_bits01(vg);
-  bf16x8 kreg[4], vreg[4];
-
-  auto load_tile = [&](int t0) {
+  // Per-lane LDS byte offsets. K (A operand of S^T = K Q^T): row l%32 of a
+  // 32-key sub-block, unit 2c + l/32. V (A operand of O^T = V^T P^T, read
+  // transposed): lane i of group g reads row 8r + 4*(g/2) + i/4 (r = 0, 1)
+  // of a 16-key step, columns 32bb + 16*(g%2) + 4*(i%4) .. +3.
+  int koff[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = t0 + kr0 + 16 * r;
-      kreg[r] = key < kend ? *(const bf16x8 *)(kbase + key * tok + 8 * kd) : zero_bf16x8();
-      const int vkey = t0 + 4 * vg + r;
-      vreg[r] = vkey < kend ? *(const bf16x8 *)(vbase + vkey * tok + 8 * vd) : zero_bf16x8();
+  for (int c = 0; c < 8; ++c) koff[c] = tile_off(l32, 2 * c + hl);
+  const int gi = lane & 15, g = lane >> 4;
+  int voff[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int row = 8 * r + 4 * (g >> 1) + (gi >> 2);
+      const int col = 32 * bb + 16 * (g & 1) + 4 * (gi & 3);
+      voff[r][bb] = tile_off(row, col >> 3) + 2 * (col & 7);
     }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) *(bf16x8 *)(Ks + (kr0 + 16 * r) * KS_LD + 8 * kd) = kreg[r];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16x4 t;
-      t[0] = vreg[0][e];
-      t[1] = vreg[1][e];
-      t[2] = vreg[2][e];
-      t[3] = vreg[3][e];
-      *(bf16x4 *)(Vt + (8 * vd + e) * VT_LD + vpos) = t;
-    }
-  };
 
-  load_tile(kbeg);
+  __builtin_amdgcn_s_waitcnt(0);  // Q operands and the first tile have landed
+  __syncthreads();
+
+  int buf = 0;
   for (int t0 = kbeg; t0 < kend; t0 += KB) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (t0 + KB < kend) load_tile(t0 + KB);
+    const char *Kc = (const char *)(buf ? Kt1 : Kt0);
+    const char *Vc = (const char *)(buf ? Vt1 : Vt0);
+    const bool more = t0 + KB < kend;
+    if (more) {
+      load_tile_regs(kbase, tok, t0 + KB, kend, tid, kreg);
+      load_tile_regs(vbase, tok, t0 + KB, kend, tid, vreg);
+    }
     const int nvalid = kend - t0;
 
     // S^T for two 32-key sub-blocks: rows = keys, columns = this wave's queries.
@@ -127,7 +172,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnKParams p) {
       s[sb] = zero16();
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const bf16x8 a = *(const bf16x8 *)(Ks + (32 * sb + l32) * KS_LD + 16 * c + 8 * hl);
+        const bf16x8 a = *(const bf16x8 *)(Kc + sb * 32 * 256 + koff[c]);
         s[sb] = mfma32(a, qop[c], s[sb]);
       }
     }
@@ -141,24 +186,27 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnKParams p) {
         }
     }
 
-    // Online softmax in the log2 domain (every tile has a valid key, so the
-    // new maximum is finite).
+    // Online softmax in the log2 domain. The running maximum is only moved
+    // when a new score exceeds it by more than 2^8; in between, exponents
+    // stay below 2^8, which fp32 sums and bf16 probabilities carry exactly
+    // as well as values below 1 (every tile has a valid key, so the first
+    // tile always sets a finite maximum).
     float mx = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float mnew = fmaxf(m, mx * p.scale);
-    if (wave_any(mnew != m)) {
+    mx = fmaxf(mx, swap_halves(mx)) * p.scale;
+    if (wave_any(mx > m + 8.f)) {
+      const float mnew = fmaxf(m, mx);
       const float r = exp2_fast(m - mnew);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[bb][i] *= r;
       lsum *= r;
+      m = mnew;
     }
-    m = mnew;
 
     bf16x8 pb[4];
     float ps = 0.f;
@@ -166,7 +214,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnKParams p) {
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = exp2_fast(fmaf(s[sb][i], p.scale, -mnew));
+        const float pv = exp2_fast(fmaf(s[sb][i], p.scale, -m));
         ps += pv;
         pb[2 * sb + (i >> 3)][i & 7] = (bf16)pv;
       }
@@ -177,9 +225,20 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnKParams p) {
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const bf16x8 a = *(const bf16x8 *)(Vt + (32 * bb + l32) * VT_LD + 16 * kk + 8 * hl);
+        const s16x4 lo = lds_read_tr16(Vc + kk * 16 * 256 + voff[0][bb]);
+        const s16x4 hi = lds_read_tr16(Vc + kk * 16 * 256 + voff[1][bb]);
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0],
+                                                                hi[1], hi[2], hi[3]});
         o[bb] = mfma32(a, pb[kk], o[bb]);
       }
+
+    if (more) {
+      store_tile_regs((char *)(buf ? Kt0 : Kt1), tid, kreg);
+      store_tile_regs((char *)(buf ? Vt0 : Vt1), tid, vreg);
+    }
+    __syncthreads();  // the next tile is in LDS and nobody reads this one any more
+    buf ^= 1;
   }
 
   const int64_t blk = (((int64_t)b * p.H + h) * p.nqblk + qblk) * p.nsplit + split;
@@ -205,9 +264,22 @@ struct CombineKParams {
   int with_inter;
 };
 
+// A operand (rows = 32 columns 32bb .. 32bb+31 of the tile, k = 8 tile
+// rows) read transposed from a swizzled row-major 128x128 bf16 tile: rows
+// k0 .. k0+3 land in elements 0..3 and rows k1 .. k1+3 in elements 4..7.
+__device__ __forceinline__ bf16x8 tile_col_operand(const char *tile, int k0, int k1, int lane,
+                                                   int bb) {
+  const int gi = lane & 15, g = lane >> 4;
+  const int col = 32 * bb + 16 * (g & 1) + 4 * (gi & 3);
+  const s16x4 lo = lds_read_tr16(tile + tile_off(k0 + (gi >> 2), col >> 3) + 2 * (col & 7));
+  const s16x4 hi = lds_read_tr16(tile + tile_off(k1 + (gi >> 2), col >> 3) + 2 * (col & 7));
+  return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                        lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
 __global__ __launch_bounds__(256) void inter_combine_kernel(CombineKParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 WqT[D * W_LD];
-  __shared__ __attribute__((aligned(16))) bf16 ST[D * W_LD];
+  __shared__ __attribute__((aligned(1024))) bf16 Wt[D * D];   // W_q[h], row-major [din][dout]
+  __shared__ __attribute__((aligned(1024))) bf16 St[D * D];   // bf16(S[b][h]), row-major [dk][dv]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
@@ -220,10 +292,29 @@ __global__ __launch_bounds__(256) void inter_combine_kernel(CombineKParams p) {
   for (int bb = 0; bb < 4; ++bb) oi[bb] = zero16();
 
   if (p.with_inter) {
-    stage_weight_T(p.Wq + (int64_t)h * D * D, WqT, tid);
-    stage_state_T(p.S + ((int64_t)b * p.H + h) * D * D, ST, nullptr, tid);
-    __syncthreads();
-
+    // W_q[h]: 32 chunks of 4 rows, copied straight into LDS (8 per wave).
+    const bf16 *W = p.Wq + (int64_t)h * D * D;
+    const int r4 = lane >> 4, pos = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int cc = 8 * wave + i, row = 4 * cc + r4;
+      global_to_lds16(W + row * D + 8 * (pos ^ tile_swz(row & 15)), Wt + cc * 512);
+    }
+    // S[b][h] rounded to bf16: thread t converts rows t/16 + 16i, unit t%16.
+    const float *Sh = p.S + ((int64_t)b * p.H + h) * D * D;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = (tid >> 4) + 16 * i, u = tid & 15;
+      const f32x4 a = *(const f32x4 *)(Sh + row * D + 8 * u);
+      const f32x4 c = *(const f32x4 *)(Sh + row * D + 8 * u + 4);
+      bf16x8 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[e] = (bf16)a[e];
+        t[4 + e] = (bf16)c[e];
+      }
+      *(bf16x8 *)((char *)St + tile_off(row, u)) = t;
+    }
     bf16x8 qop[8];
     if (qrow < p.L) {
       const bf16 *qp = p.q + ((int64_t)b * p.L * p.H + h) * D + qrow * tok + 8 * hl;
@@ -233,16 +324,19 @@ __global__ __launch_bounds__(256) void inter_combine_kernel(CombineKParams p) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) qop[c] = zero_bf16x8();
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
     // (q W_q)^T = W_q^T q^T: lane = query, registers = output features.
     f32x16 qp4[4];
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
       qp4[bb] = zero16();
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const bf16x8 a = *(const bf16x8 *)(WqT + (32 * bb + l32) * W_LD + 16 * c + 8 * hl);
-        qp4[bb] = mfma32(a, qop[c], qp4[bb]);
-      }
+      for (int c = 0; c < 8; ++c)
+        qp4[bb] = mfma32(tile_col_operand((const char *)Wt, 16 * c + 8 * hl, 16 * c + 8 * hl + 4,
+                                          lane, bb),
+                         qop[c], qp4[bb]);
     }
     float ss = 0.f;
 #pragma unroll
@@ -251,17 +345,19 @@ __global__ __launch_bounds__(256) void inter_combine_kernel(CombineKParams p) {
       for (int i = 0; i < 16; ++i) ss = fmaf(qp4[bb][i], qp4[bb][i], ss);
     ss += swap_halves(ss);
     const float inv = 1.f / fmaxf(sqrtf(ss), kL2Eps);
-    // O_inter^T = S^T Q'^T with Q' fed straight from the accumulators.
+    // O_inter^T = S^T Q'^T, Q' fed straight from the accumulators: register
+    // 8*(g%2) + j of block g/2 holds feature 16g + swap_bits23(8*(l/32) + j),
+    // i.e. rows 16g + 4*(l/32) + {0..3} and 16g + 8 + 4*(l/32) + {0..3}.
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       bf16x8 qb;
 #pragma unroll
       for (int j = 0; j < 8; ++j) qb[j] = (bf16)(qp4[g >> 1][8 * (g & 1) + j] * inv);
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const bf16x8 a = *(const bf16x8 *)(ST + (32 * bb + l32) * W_LD + 16 * g + 8 * hl);
-        oi[bb] = mfma32(a, qb, oi[bb]);
-      }
+      for (int bb = 0; bb < 4; ++bb)
+        oi[bb] = mfma32(
+            tile_col_operand((const char *)St, 16 * g + 4 * hl, 16 * g + 8 + 4 * hl, lane, bb), qb,
+            oi[bb]);
     }
   }
 
@@ -306,9 +402,9 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
   AttnPlan pl;
   pl.nqblk = (int)((Lq + kQBlock - 1) / kQBlock);
   const int64_t base = B * H * pl.nqblk;
-  // Enough workgroups to cover the 256 compute units about twice, without
-  // splitting a key range below two tiles.
-  int64_t ns = (448 + base - 1) / base;
+  // Two workgroups fit on a compute unit: aim for at most 2 x 256 work
+  // items, without splitting a key range below two tiles.
+  int64_t ns = 512 / base;
   const int64_t max_by_keys = (Lk + 2 * kKeyTile - 1) / (2 * kKeyTile);
   if (ns > max_by_keys) ns = max_by_keys;
   if (ns > 16) ns = 16;
@@ -334,8 +430,9 @@ hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s) {
   p.ws_o = a.ws_o;
   p.ws_ml = a.ws_ml;
   p.scale = kLog2e / sqrtf((float)D);
-  dim3 grid((unsigned)(a.plan.nqblk * a.plan.nsplit), (unsigned)a.H, (unsigned)a.B);
-  hipLaunchKernelGGL(attn_partial_kernel, grid, dim3(256), 0, s, p);
+  p.nitems = a.B * a.H * a.plan.nsplit * a.plan.nqblk;
+  p.per_xcd = (p.nitems + 7) / 8;
+  hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)(8 * p.per_xcd)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -156,6 +156,20 @@ ARL2_API arl2_status arl2_softmax_attention(const void *q, const void *kc, const
                                    int32_t H, int32_t d, int32_t Lq, int32_t Lk, int32_t dtype,
                                    void *out, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Kernel timing (diagnostics). While enabled, every kernel the library
+ * launches is bracketed by a pair of hipEvents recorded on the launch stream;
+ * arl2_profile_report waits for the recorded events and writes one line per
+ * kernel, "<name> <launches> <total_ms>\n", into buf (NUL-terminated,
+ * truncated to len). Disabled by default; event records add a small gap
+ * between launches while enabled. Not for use under graph capture.
+ * Errors: INVALID_ARG for a NULL buf or len 0; ARL2_ERR_HIP if an event
+ * cannot be created or queried.
+ */
+ARL2_API arl2_status arl2_profile_enable(int32_t on);
+ARL2_API arl2_status arl2_profile_report(char *buf, size_t len);
+ARL2_API void arl2_profile_reset(void);
+
 /* Static text for a status code (never NULL). */
 ARL2_API const char *arl2_status_string(int32_t status);
 

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert {"arl2_state_init", "arl2_state_reset", "arl2_frame_forward",
             "arl2_workspace_bytes"} <= names
-    assert len(names) == 9
+    assert len(names) == 12
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -43,6 +43,12 @@ def test_library_exports_every_declared_symbol(B):
     # nothing else with the public prefix leaks out
     assert {e for e in exported if e.startswith("arl2_")} == _declared()
     assert set(B.EXPORTED) == _declared()
+
+
+def test_profile_report_without_launches(B):
+    B.arl2_profile_reset()
+    assert B.arl2_profile_report() == {}
+    B.arl2_profile_enable(False)
 
 
 def test_version_and_status_strings(B):

@@ -100,7 +100,20 @@ def main() -> int:
                     choices=["frame_step_480p", "stream21_480p", "batched720p"])
     ap.add_argument("--profile-steps", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only copy a buffer of this many MiB 10 times (scales the HBM byte "
+                         "counters of a profiler run) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy_mib:
+        import torch
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copied_bytes_per_launch": n, "launches": 10}))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(heads and streams shard with no exchange; see the sharding note in the design)",

@@ -88,6 +88,36 @@ __device__ __forceinline__ void global_to_lds16(const void *gsrc, void *lds_base
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t *)lds_base, 16, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes from `base` (raw, no stride): loads at
+// offsets past the end return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// Buffer -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// lds_base + 16 * i (lds_base uniform across the wavefront); dwords past the
+// resource's end are written as zeros.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void *lds_base, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, voff, 0, 0, 0);
+}
+
+// Sum of the eight bf16 values of v added to acc (fp32, exact products).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+
 // Split an fp32 value into bf16 high and low parts, x ~= hi + lo (the
 // three-product bf16 scheme of Henry, Tang and Heinecke, ARITH 2019).
 __device__ __forceinline__ void split_bf16(float x, bf16 &hi, bf16 &lo) {

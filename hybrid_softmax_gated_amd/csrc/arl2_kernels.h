@@ -10,48 +10,49 @@ namespace arl2 {
 
 // ---------------------------------------------------------------- plans
 // How one attention call is cut into workgroups: query blocks of 128 rows
-// (4 wavefronts x 32 queries) and `nsplit` contiguous key ranges of
-// `keys_per_split` keys (a multiple of the 64-key tile). Partial results of
-// the key ranges are merged by the combine kernel.
+// (4 wavefronts x 32 queries) and `nsplit` contiguous key ranges: the first
+// holds `kps0` keys, the others `keys_per_split` (multiples of the 64-key
+// tile). Partial results of the key ranges are merged by the merge kernel.
 struct AttnPlan {
   int nqblk = 0;
   int nsplit = 0;
+  int kps0 = 0;
   int keys_per_split = 0;
 };
 
 constexpr int kQBlock = 128;      // queries per attention workgroup
 constexpr int kKeyTile = 64;      // keys per LDS tile
+constexpr int kInterKeys = 128;   // keys the first range gives up for the inter-frame read
 constexpr int kDeltaChunk = 128;  // tokens per delta-update workgroup (MFMA path)
 constexpr int kGenChunk = 32;     // tokens per delta-update workgroup (generic path)
 
-AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk);
+AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk, bool inter);
 
-// Floats of partial output per (stream, head, query block, split): 4 waves x
-// 64 accumulator registers x 64 lanes; and of row statistics (max, sum).
-constexpr int64_t kPartialO = 4 * 64 * 64;
-constexpr int64_t kPartialML = 4 * 64;
+// Floats of partial output per (stream, head, query block, split): O[128][128]
+// and (max, sum)[128].
+constexpr int64_t kPartialO = 128 * 128;
+constexpr int64_t kPartialML = 128 * 2;
 
 // ---------------------------------------------------------------- MFMA path
 // bf16 io, d = 128.
 struct AttnArgs {
   const void *q, *k, *v;  // [B][Lq][H][128], [B][Lk][H][128]
+  const void *Wq;         // [H][128][128] (read when ws_inter is set)
+  const float *S;         // [B][H][128][128] (read when ws_inter is set)
   int B, H, Lq, Lk;
   AttnPlan plan;
   float *ws_o, *ws_ml;
+  float *ws_inter;        // [B][H][nqblk*128][128] O_inter, or null for plain attention
 };
 hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s);
 
-struct CombineArgs {
-  const void *q;     // [B][L][H][128] (read only when with_inter)
-  const void *Wq;    // [H][128][128]
-  const float *S;    // [B][H][128][128]
+struct MergeArgs {
+  const float *ws_o, *ws_ml, *ws_inter;  // ws_inter may be null
   int B, H, L;
   AttnPlan plan;
-  const float *ws_o, *ws_ml;
-  void *out;         // [B][L][H][128]
-  bool with_inter;
+  void *out;  // [B][L][H][128] bf16
 };
-hipError_t launch_inter_combine_bf16(const CombineArgs &a, hipStream_t s);
+hipError_t launch_merge_bf16(const MergeArgs &a, hipStream_t s);
 
 struct DeltaArgs {
   const void *k, *v;     // [B][L][H][128]

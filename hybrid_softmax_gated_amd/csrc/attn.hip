@@ -13,36 +13,47 @@
 // one head are H*256 bytes apart.
 //
 // Attention kernel (one workgroup = 4 wavefronts = 128 queries of one head,
-// one contiguous key range):
+// one contiguous key range; two workgroups per compute unit):
 //  * each wavefront keeps its 32 queries in registers as MFMA B operands and
 //    computes the transposed score tile S^T = K Q^T (keys on rows), so every
 //    lane owns one query: the row max and row sum of the online softmax are
 //    in-register reductions plus one exchange between the wave halves;
-//  * K tiles are staged in LDS row-major, V tiles transposed (head dim on
-//    rows) with keys in the swap_bits23 order, so that the softmax
-//    probabilities leave the score accumulators and enter O^T = V^T P^T as
-//    the B operand without any data movement;
-//  * the next tile's global loads are issued before the current tile's
-//    MFMAs (register double buffering);
-//  * the unnormalised O^T, the row max (log2 domain) and the row sum are
-//    written per key range; the epilogue merges the ranges.
+//  * K and V tiles of 64 keys are staged in LDS row-major with a 16-byte
+//    XOR swizzle (no bank conflicts for either read pattern); V is read as
+//    the A operand of O^T = V^T P^T with the LDS transpose read, in the key
+//    order that lets the softmax probabilities leave the score accumulators
+//    and enter the next MFMA as its B operand with no data movement;
+//  * double-buffered tiles: the next tile's buffer loads are issued before
+//    the current tile's MFMAs and written to LDS after them (one barrier per
+//    tile); the loop is unrolled by two so every LDS address is a constant
+//    offset from a per-lane register;
+//  * the workgroups of the first key range also compute the inter-frame
+//    read O_inter = L2norm(q W_q) S_{N-1} for their queries before their key
+//    loop (that range is shorter by the equivalent work);
+//  * the unnormalised O, the row max (log2 domain) and the row sum are
+//    written per key range; a streaming kernel merges the ranges, adds
+//    O_inter and writes the output.
 #include "arl2_device.h"
 #include "arl2_kernels.h"
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace arl2 {
 namespace {
 
 constexpr int D = 128;
-constexpr int KB = kKeyTile;  // 64 keys per LDS tile
+constexpr int KB = kKeyTile;         // 64 keys per LDS tile
+constexpr int TILE_BYTES = KB * D * 2;  // 16 KB
 
 struct AttnKParams {
-  const bf16 *q, *k, *v;
-  int H, Lq, Lk, nsplit, kps, nqblk;
+  const bf16 *q, *k, *v, *Wq;
+  const float *S;
+  int H, Lq, Lk, nsplit, kps0, kps, nqblk;
   int nitems, per_xcd;  // work items and items per XCD (see item_of)
-  float *ws_o, *ws_ml;
-  float scale;  // log2(e) / sqrt(d)
+  float *ws_o, *ws_ml, *ws_inter;  // ws_inter null: no inter-frame read
+  float scale;                     // log2(e) / sqrt(d)
 };
 
 // Work items are (stream, head, split, query block) with the query block
@@ -54,43 +65,68 @@ __device__ __forceinline__ int item_of(int bid, int per_xcd) {
   return (bid & 7) * per_xcd + (bid >> 3);
 }
 
-// Issue the direct global->LDS copy of one 64-key tile (64 rows of 256 B,
-// swizzled): 16 chunks of 4 rows, 4 per wavefront. Rows past the key range
-// re-read the last valid row (finite values; their scores are masked).
-__device__ __forceinline__ void issue_tile(const bf16 *__restrict__ base, int64_t tok, int t0,
-                                           int kend, bf16 *tile, int wave, int lane) {
-  const int r4 = lane >> 4, pos = lane & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int cc = 4 * wave + i;
-    const int row = 4 * cc + r4;
-    const int key = min(t0 + row, kend - 1);
-    const int unit = pos ^ tile_swz(row & 15);
-    global_to_lds16(base + key * tok + 8 * unit, tile + cc * 512);
-  }
+// A operand (rows = 32 columns 32bb .. 32bb+31 of the tile, k = 8 tile
+// rows) read transposed from a swizzled row-major 128-column bf16 tile: rows
+// k0 .. k0+3 land in elements 0..3 and rows k1 .. k1+3 in elements 4..7.
+__device__ __forceinline__ bf16x8 tile_col_operand(const char *tile, int k0, int k1, int lane,
+                                                   int bb) {
+  const int gi = lane & 15, g = lane >> 4;
+  const int col = 32 * bb + 16 * (g & 1) + 4 * (gi & 3);
+  const s16x4 lo = lds_read_tr16(tile + tile_off(k0 + (gi >> 2), col >> 3) + 2 * (col & 7));
+  const s16x4 hi = lds_read_tr16(tile + tile_off(k1 + (gi >> 2), col >> 3) + 2 * (col & 7));
+  return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                        lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
-// Register-staged copy of one 64-key tile into the same swizzled layout:
-// thread t owns rows t/16 + 16i (i = 0..3), unit t%16.
-__device__ __forceinline__ void load_tile_regs(const bf16 *__restrict__ base, int64_t tok, int t0,
-                                               int kend, int tid, bf16x8 (&r)[4]) {
+// O_inter for the wavefront's 32 queries (lane = query, registers = d_v),
+// from W_q[h] (rows 0..63 in W0, 64..127 in W1) and bf16(S) (rows 0..63 in
+// S0, 64..127 in S1), each half a swizzled 64-row tile in LDS:
+// (q W_q)^T = W_q^T q^T, Q' = its columns scaled to unit length, then
+// O_inter^T = S^T Q'^T with Q' fed straight from the accumulators: register
+// 8*(g%2) + j of block g/2 holds feature 16g + swap_bits23(8*(l/32) + j),
+// i.e. rows 16g + 4*(l/32) + {0..3} and 16g + 8 + 4*(l/32) + {0..3} of S.
+__device__ __forceinline__ void inter_read_wave(const char *W0, const char *W1, const char *S0,
+                                                const char *S1, const bf16x8 (&qop)[8], int lane,
+                                                f32x16 (&oi)[4]) {
+  const int hl = lane >> 5;
+  f32x16 qp4[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = min(t0 + (tid >> 4) + 16 * i, kend - 1);
-    r[i] = *(const bf16x8 *)(base + key * tok + 8 * (tid & 15));
+  for (int bb = 0; bb < 4; ++bb) {
+    qp4[bb] = zero16();
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int k0 = (16 * c + 8 * hl) & 63;
+      qp4[bb] = mfma32(tile_col_operand(c < 4 ? W0 : W1, k0, k0 + 4, lane, bb), qop[c], qp4[bb]);
+    }
   }
-}
-__device__ __forceinline__ void store_tile_regs(char *tile, int tid, const bf16x8 (&r)[4]) {
+  float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *(bf16x8 *)(tile + tile_off((tid >> 4) + 16 * i, tid & 15)) = r[i];
+  for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss = fmaf(qp4[bb][i], qp4[bb][i], ss);
+  ss += swap_halves(ss);
+  const float inv = 1.f / fmaxf(sqrtf(ss), kL2Eps);
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) oi[bb] = zero16();
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    bf16x8 qb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qb[j] = (bf16)(qp4[g >> 1][8 * (g & 1) + j] * inv);
+    const int k0 = (16 * g + 4 * hl) & 63;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+      oi[bb] = mfma32(tile_col_operand(g < 4 ? S0 : S1, k0, k0 + 8, lane, bb), qb, oi[bb]);
+  }
 }
 
 __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
-  __shared__ __attribute__((aligned(1024))) bf16 Kt0[KB * D];
-  __shared__ __attribute__((aligned(1024))) bf16 Kt1[KB * D];
-  __shared__ __attribute__((aligned(1024))) bf16 Vt0[KB * D];
-  __shared__ __attribute__((aligned(1024))) bf16 Vt1[KB * D];
+  // Double-buffered K and V tiles, each its own array so that the compiler
+  // sees the copies into one buffer and the reads of the other as disjoint.
+  __shared__ __attribute__((aligned(1024))) char Ks0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ks1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Vs0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Vs1[TILE_BYTES];
 
   const int item = item_of(blockIdx.x, p.per_xcd);
   if (item >= p.nitems) return;
@@ -102,18 +138,36 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-  const int64_t tok = (int64_t)p.H * D;
+  const int64_t tok = (int64_t)p.H * D;     // elements between tokens
+  const int64_t tokB = tok * 2;             // bytes between tokens
   const bf16 *qbase = p.q + ((int64_t)b * p.Lq * p.H + h) * D;
-  const bf16 *kbase = p.k + ((int64_t)b * p.Lk * p.H + h) * D;
-  const bf16 *vbase = p.v + ((int64_t)b * p.Lk * p.H + h) * D;
-  const int kbeg = split * p.kps;
-  const int kend = min(p.Lk, kbeg + p.kps);
+  const char *kbase = (const char *)(p.k + ((int64_t)b * p.Lk * p.H + h) * D);
+  const char *vbase = (const char *)(p.v + ((int64_t)b * p.Lk * p.H + h) * D);
+  const int kbeg = split == 0 ? 0 : p.kps0 + (split - 1) * p.kps;
+  const int kend = min(p.Lk, split == 0 ? p.kps0 : kbeg + p.kps);
 
-  bf16x8 kreg[4], vreg[4];
-  load_tile_regs(kbase, tok, kbeg, kend, tid, kreg);
-  load_tile_regs(vbase, tok, kbeg, kend, tid, vreg);
-  store_tile_regs((char *)Kt0, tid, kreg);
-  store_tile_regs((char *)Vt0, tid, vreg);
+  // Tile copies: wavefront w copies chunks 4w .. 4w+3 of 4 rows (1 KB) each;
+  // lane (r4 = l/16, pos = l%16) of chunk cc fetches row 4cc + r4, 16-byte
+  // unit pos ^ swizzle, so the bytes land in the swizzled layout.
+  int doff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (4 * wave + i) + (lane >> 4);
+    doff[i] = (int)(row * tokB) + 16 * ((lane & 15) ^ tile_swz(row & 15));
+  }
+  // Copy the tile starting at key t0 into (kt, vt); rows at or past kend
+  // read as zeros.
+  auto copy_tile = [&](int t0, char *kt, char *vt) {
+    const int64_t span = (int64_t)(kend - t0) * tokB;
+    const uint32_t n = (uint32_t)(span < (int64_t)0x7fffffff ? span : (int64_t)0x7fffffff);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + t0 * tokB, n);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + t0 * tokB, n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      buffer_to_lds16(rk, kt + (4 * wave + i) * 1024, doff[i]);
+      buffer_to_lds16(rv, vt + (4 * wave + i) * 1024, doff[i]);
+    }
+  };
 
   // The wavefront's 32 queries as B operands: lane l holds query l%32,
   // head-dim elements 16c + 8*(l/32) .. +7.
@@ -127,6 +181,51 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) qop[c] = zero_bf16x8();
   }
+
+  if (split == 0 && p.ws_inter) {
+    // W_q[h] rows 0..63 in Ks0, 64..127 in Ks1 (copied straight into LDS);
+    // bf16(S[b][h]) rows 0..63 in Vs0, 64..127 in Vs1.
+    const bf16 *W = p.Wq + (int64_t)h * D * D;
+    const int r4 = lane >> 4, pos = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int cc = 8 * wave + i, row = 4 * cc + r4;
+      global_to_lds16(W + row * D + 8 * (pos ^ tile_swz(row & 15)),
+                      (cc < 16 ? Ks0 : Ks1) + (cc & 15) * 1024);
+    }
+    const float *Sh = p.S + ((int64_t)b * p.H + h) * D * D;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = (tid >> 4) + 16 * i, u = tid & 15;
+      const f32x4 a = *(const f32x4 *)(Sh + row * D + 8 * u);
+      const f32x4 c = *(const f32x4 *)(Sh + row * D + 8 * u + 4);
+      bf16x8 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[e] = (bf16)a[e];
+        t[4 + e] = (bf16)c[e];
+      }
+      *(bf16x8 *)((i < 4 ? Vs0 : Vs1) + tile_off(row & 63, u)) = t;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 oi[4];
+    inter_read_wave(Ks0, Ks1, Vs0, Vs1, qop, lane, oi);
+    float *dst = p.ws_inter + (((int64_t)b * p.H + h) * p.nqblk * kQBlock + qblk * kQBlock +
+                               wave * 32 + l32) * D;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = oi[bb][4 * r + e];
+        *(f32x4 *)(dst + 32 * bb + 8 * r + 4 * hl) = t;
+      }
+    __syncthreads();  // LDS is free for the key tiles
+  }
+
+  copy_tile(kbeg, Ks0, Vs0);
 
   f32x16 o[4];
 #pragma unroll
@@ -154,28 +253,28 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
   __builtin_amdgcn_s_waitcnt(0);  // Q operands and the first tile have landed
   __syncthreads();
 
-  int buf = 0;
-  for (int t0 = kbeg; t0 < kend; t0 += KB) {
-    const char *Kc = (const char *)(buf ? Kt1 : Kt0);
-    const char *Vc = (const char *)(buf ? Vt1 : Vt0);
+  // One 64-key tile from buffer BUF; the next tile is copied into the other
+  // buffer meanwhile. Returns false after the last tile.
+  auto step = [&](auto bufc, int t0) -> bool {
+    constexpr int BUF = decltype(bufc)::value;
+    const char *Kc = BUF ? Ks1 : Ks0;
+    const char *Vc = BUF ? Vs1 : Vs0;
     const bool more = t0 + KB < kend;
-    if (more) {
-      load_tile_regs(kbase, tok, t0 + KB, kend, tid, kreg);
-      load_tile_regs(vbase, tok, t0 + KB, kend, tid, vreg);
-    }
+    if (more) copy_tile(t0 + KB, BUF ? Ks0 : Ks1, BUF ? Vs0 : Vs1);
     const int nvalid = kend - t0;
 
-    // S^T for two 32-key sub-blocks: rows = keys, columns = this wave's queries.
+    // S^T for two 32-key sub-blocks (rows = keys, columns = this wave's
+    // queries), as two interleaved accumulation chains.
     f32x16 s[2];
+    s[0] = zero16();
+    s[1] = zero16();
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      s[sb] = zero16();
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int sb = 0; sb < 2; ++sb) {
         const bf16x8 a = *(const bf16x8 *)(Kc + sb * 32 * 256 + koff[c]);
         s[sb] = mfma32(a, qop[c], s[sb]);
       }
-    }
     if (nvalid < KB) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -209,16 +308,16 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
     }
 
     bf16x8 pb[4];
-    float ps = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = exp2_fast(fmaf(s[sb][i], p.scale, -m));
-        ps += pv;
-        pb[2 * sb + (i >> 3)][i & 7] = (bf16)pv;
-      }
-    lsum += ps;
+      for (int i = 0; i < 16; ++i)
+        pb[2 * sb + (i >> 3)][i & 7] = (bf16)exp2_fast(fmaf(s[sb][i], p.scale, -m));
+    // Row sums of the rounded probabilities (the values the MFMAs consume).
+    float ps[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) ps[kk] = sum_bf16x8(pb[kk], 0.f);
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
     // O^T += V^T P^T over the tile's 64 keys (4 steps of 16).
 #pragma unroll
@@ -233,172 +332,80 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
         o[bb] = mfma32(a, pb[kk], o[bb]);
       }
 
-    if (more) {
-      store_tile_regs((char *)(buf ? Kt0 : Kt1), tid, kreg);
-      store_tile_regs((char *)(buf ? Vt0 : Vt1), tid, vreg);
-    }
-    __syncthreads();  // the next tile is in LDS and nobody reads this one any more
-    buf ^= 1;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
+    __syncthreads();                // everyone's have, and nobody reads this tile any more
+    return more;
+  };
+
+  for (int t0 = kbeg;; t0 += 2 * KB) {
+    if (!step(std::integral_constant<int, 0>(), t0)) break;
+    if (!step(std::integral_constant<int, 1>(), t0 + KB)) break;
   }
 
+  // Partial results in natural layout: O[query][d] (unnormalised), (m, l).
   const int64_t blk = (((int64_t)b * p.H + h) * p.nqblk + qblk) * p.nsplit + split;
-  float *wo = p.ws_o + blk * kPartialO + wave * 64 * 64;
+  float *wo = p.ws_o + blk * kPartialO + (wave * 32 + l32) * D;
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) wo[(16 * bb + i) * 64 + lane] = o[bb][i];
+    for (int r = 0; r < 4; ++r) {
+      f32x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = o[bb][4 * r + e];
+      *(f32x4 *)(wo + 32 * bb + 8 * r + 4 * hl) = t;
+    }
   const float lt = lsum + swap_halves(lsum);
-  float *wml = p.ws_ml + blk * kPartialML + wave * 64;
   if (hl == 0) {
-    wml[l32] = m;
-    wml[32 + l32] = lt;
+    float *wml = p.ws_ml + blk * kPartialML + 2 * (wave * 32 + l32);
+    wml[0] = m;
+    wml[1] = lt;
   }
 }
 
-struct CombineKParams {
-  const bf16 *q, *Wq;
-  const float *S;
+struct MergeKParams {
+  const float *ws_o, *ws_ml, *ws_inter;  // ws_inter may be null
   int H, L, nqblk, nsplit;
-  const float *ws_o, *ws_ml;
   bf16 *out;
-  int with_inter;
 };
 
-// A operand (rows = 32 columns 32bb .. 32bb+31 of the tile, k = 8 tile
-// rows) read transposed from a swizzled row-major 128x128 bf16 tile: rows
-// k0 .. k0+3 land in elements 0..3 and rows k1 .. k1+3 in elements 4..7.
-__device__ __forceinline__ bf16x8 tile_col_operand(const char *tile, int k0, int k1, int lane,
-                                                   int bb) {
-  const int gi = lane & 15, g = lane >> 4;
-  const int col = 32 * bb + 16 * (g & 1) + 4 * (gi & 3);
-  const s16x4 lo = lds_read_tr16(tile + tile_off(k0 + (gi >> 2), col >> 3) + 2 * (col & 7));
-  const s16x4 hi = lds_read_tr16(tile + tile_off(k1 + (gi >> 2), col >> 3) + 2 * (col & 7));
-  return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
-                                        lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-}
-
-__global__ __launch_bounds__(256) void inter_combine_kernel(CombineKParams p) {
-  __shared__ __attribute__((aligned(1024))) bf16 Wt[D * D];   // W_q[h], row-major [din][dout]
-  __shared__ __attribute__((aligned(1024))) bf16 St[D * D];   // bf16(S[b][h]), row-major [dk][dv]
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-  const int qblk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int64_t tok = (int64_t)p.H * D;
-  const int qrow = qblk * kQBlock + wave * 32 + l32;
-
-  f32x16 oi[4];  // O_inter^T: lane = query, registers = d_v
-#pragma unroll
-  for (int bb = 0; bb < 4; ++bb) oi[bb] = zero16();
-
-  if (p.with_inter) {
-    // W_q[h]: 32 chunks of 4 rows, copied straight into LDS (8 per wave).
-    const bf16 *W = p.Wq + (int64_t)h * D * D;
-    const int r4 = lane >> 4, pos = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int cc = 8 * wave + i, row = 4 * cc + r4;
-      global_to_lds16(W + row * D + 8 * (pos ^ tile_swz(row & 15)), Wt + cc * 512);
-    }
-    // S[b][h] rounded to bf16: thread t converts rows t/16 + 16i, unit t%16.
-    const float *Sh = p.S + ((int64_t)b * p.H + h) * D * D;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 4) + 16 * i, u = tid & 15;
-      const f32x4 a = *(const f32x4 *)(Sh + row * D + 8 * u);
-      const f32x4 c = *(const f32x4 *)(Sh + row * D + 8 * u + 4);
-      bf16x8 t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t[e] = (bf16)a[e];
-        t[4 + e] = (bf16)c[e];
-      }
-      *(bf16x8 *)((char *)St + tile_off(row, u)) = t;
-    }
-    bf16x8 qop[8];
-    if (qrow < p.L) {
-      const bf16 *qp = p.q + ((int64_t)b * p.L * p.H + h) * D + qrow * tok + 8 * hl;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) qop[c] = *(const bf16x8 *)(qp + 16 * c);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) qop[c] = zero_bf16x8();
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // (q W_q)^T = W_q^T q^T: lane = query, registers = output features.
-    f32x16 qp4[4];
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      qp4[bb] = zero16();
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        qp4[bb] = mfma32(tile_col_operand((const char *)Wt, 16 * c + 8 * hl, 16 * c + 8 * hl + 4,
-                                          lane, bb),
-                         qop[c], qp4[bb]);
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ss = fmaf(qp4[bb][i], qp4[bb][i], ss);
-    ss += swap_halves(ss);
-    const float inv = 1.f / fmaxf(sqrtf(ss), kL2Eps);
-    // O_inter^T = S^T Q'^T, Q' fed straight from the accumulators: register
-    // 8*(g%2) + j of block g/2 holds feature 16g + swap_bits23(8*(l/32) + j),
-    // i.e. rows 16g + 4*(l/32) + {0..3} and 16g + 8 + 4*(l/32) + {0..3}.
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      bf16x8 qb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qb[j] = (bf16)(qp4[g >> 1][8 * (g & 1) + j] * inv);
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb)
-        oi[bb] = mfma32(
-            tile_col_operand((const char *)St, 16 * g + 4 * hl, 16 * g + 8 + 4 * hl, lane, bb), qb,
-            oi[bb]);
-    }
-  }
-
-  // Merge the key-range partials of the intra-frame branch.
-  const int64_t blk0 = (((int64_t)b * p.H + h) * p.nqblk + qblk) * p.nsplit;
+// out = (sum_s 2^(m_s - M) O_s) / (sum_s 2^(m_s - M) l_s) + O_inter, one
+// thread per (query, 4 consecutive head-dim values): a workgroup covers 8
+// queries of one query block, each row written as 256 contiguous bytes.
+__global__ __launch_bounds__(256) void merge_kernel(MergeKParams p) {
+  const int grp = blockIdx.x & 15;   // 8-query group within the 128-query block
+  const int blkq = blockIdx.x >> 4;  // (b, h, qblk)
+  const int qi = grp * 8 + (threadIdx.x >> 5), c = threadIdx.x & 31;
+  const int qblk = blkq % p.nqblk;
+  const int bh = blkq / p.nqblk;
+  const int h = bh % p.H, b = bh / p.H;
+  const int qrow = qblk * kQBlock + qi;
+  if (qrow >= p.L) return;
+  const int64_t blk0 = (int64_t)blkq * p.nsplit;
   float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s)
-    M = fmaxf(M, p.ws_ml[(blk0 + s) * kPartialML + wave * 64 + l32]);
-  f32x16 o[4];
-#pragma unroll
-  for (int bb = 0; bb < 4; ++bb) o[bb] = zero16();
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, p.ws_ml[(blk0 + s) * kPartialML + 2 * qi]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float Lt = 0.f;
   for (int s = 0; s < p.nsplit; ++s) {
-    const float *ml = p.ws_ml + (blk0 + s) * kPartialML + wave * 64;
-    const float w = exp2_fast(ml[l32] - M);
-    Lt = fmaf(w, ml[32 + l32], Lt);
-    const float *po = p.ws_o + (blk0 + s) * kPartialO + wave * 64 * 64 + lane;
+    const float *ml = p.ws_ml + (blk0 + s) * kPartialML + 2 * qi;
+    const float w = exp2_fast(ml[0] - M);
+    Lt = fmaf(w, ml[1], Lt);
+    const f32x4 v = *(const f32x4 *)(p.ws_o + (blk0 + s) * kPartialO + qi * D + 4 * c);
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[bb][i] = fmaf(w, po[(16 * bb + i) * 64], o[bb][i]);
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, v[e], acc[e]);
   }
-  const float invl = 1.f / Lt;
-
-  if (qrow < p.L) {
-    bf16 *op = p.out + ((int64_t)b * p.L * p.H + h) * D + qrow * tok;
+  const float inv = 1.f / Lt;
+  f32x4 add = {0.f, 0.f, 0.f, 0.f};
+  if (p.ws_inter)
+    add = *(const f32x4 *)(p.ws_inter + ((int64_t)bh * p.nqblk * kQBlock + qrow) * D + 4 * c);
+  bf16x4 t;
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bf16x4 t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = (bf16)fmaf(o[bb][4 * r + e], invl, oi[bb][4 * r + e]);
-        *(bf16x4 *)(op + 32 * bb + 8 * r + 4 * hl) = t;
-      }
-  }
+  for (int e = 0; e < 4; ++e) t[e] = (bf16)fmaf(acc[e], inv, add[e]);
+  *(bf16x4 *)(p.out + (((int64_t)b * p.L + qrow) * p.H + h) * D + 4 * c) = t;
 }
 
 }  // namespace
 
-AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
+AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk, bool inter) {
   AttnPlan pl;
   pl.nqblk = (int)((Lq + kQBlock - 1) / kQBlock);
   const int64_t base = B * H * pl.nqblk;
@@ -409,10 +416,15 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
   if (ns > max_by_keys) ns = max_by_keys;
   if (ns > 16) ns = 16;
   if (ns < 1) ns = 1;
-  int64_t kps = (Lk + ns - 1) / ns;
+  // The first range is shorter by the inter-frame read's share of work.
+  const int64_t shift = (inter && ns > 1) ? kInterKeys : 0;
+  int64_t kps = (Lk + shift + ns - 1) / ns;
   kps = (kps + kKeyTile - 1) / kKeyTile * kKeyTile;
+  int64_t kps0 = kps - shift;
+  if (kps0 < kKeyTile) kps0 = kKeyTile;
+  pl.kps0 = (int)kps0;
   pl.keys_per_split = (int)kps;
-  pl.nsplit = (int)((Lk + kps - 1) / kps);  // every split holds at least one key
+  pl.nsplit = Lk <= kps0 ? 1 : (int)(1 + (Lk - kps0 + kps - 1) / kps);
   return pl;
 }
 
@@ -421,14 +433,18 @@ hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s) {
   p.q = (const bf16 *)a.q;
   p.k = (const bf16 *)a.k;
   p.v = (const bf16 *)a.v;
+  p.Wq = (const bf16 *)a.Wq;
+  p.S = a.S;
   p.H = a.H;
   p.Lq = a.Lq;
   p.Lk = a.Lk;
   p.nsplit = a.plan.nsplit;
+  p.kps0 = a.plan.kps0;
   p.kps = a.plan.keys_per_split;
   p.nqblk = a.plan.nqblk;
   p.ws_o = a.ws_o;
   p.ws_ml = a.ws_ml;
+  p.ws_inter = a.ws_inter;
   p.scale = kLog2e / sqrtf((float)D);
   p.nitems = a.B * a.H * a.plan.nsplit * a.plan.nqblk;
   p.per_xcd = (p.nitems + 7) / 8;
@@ -436,21 +452,18 @@ hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_inter_combine_bf16(const CombineArgs &a, hipStream_t s) {
-  CombineKParams p;
-  p.q = (const bf16 *)a.q;
-  p.Wq = (const bf16 *)a.Wq;
-  p.S = a.S;
+hipError_t launch_merge_bf16(const MergeArgs &a, hipStream_t s) {
+  MergeKParams p;
+  p.ws_o = a.ws_o;
+  p.ws_ml = a.ws_ml;
+  p.ws_inter = a.ws_inter;
   p.H = a.H;
   p.L = a.L;
   p.nqblk = a.plan.nqblk;
   p.nsplit = a.plan.nsplit;
-  p.ws_o = a.ws_o;
-  p.ws_ml = a.ws_ml;
   p.out = (bf16 *)a.out;
-  p.with_inter = a.with_inter ? 1 : 0;
-  dim3 grid((unsigned)a.plan.nqblk, (unsigned)a.H, (unsigned)a.B);
-  hipLaunchKernelGGL(inter_combine_kernel, grid, dim3(256), 0, s, p);
+  const int64_t blocks = (int64_t)a.B * a.H * a.plan.nqblk * 16;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

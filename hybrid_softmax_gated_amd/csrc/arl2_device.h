@@ -23,6 +23,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16) += A(16x32) * B(32x16), bf16 operands, fp32 accumulation. Lane l
+// supplies A[row = l%16][k = 8*(l/16) .. +7] and B[k = 8*(l/16) .. +7]
+// [col = l%16]; accumulator register i of lane l holds
+// D[row = 4*(l/16) + i][col = l%16].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
 // Accumulator rows come in the order 8*(i/4) + 4*(l/32) + i%4; an operand's
 // k index runs 8*(l/32) + j. Within a group of 16, row r of an accumulator
 // therefore lines up with operand position swap_bits23(r): registers
@@ -92,9 +105,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource over `bytes` bytes from `base` (raw, no stride): loads at
-// offsets past the end return zeros instead of touching memory.
+// offsets past the end return zeros instead of touching memory. Both
+// arguments must be the same on every lane; they are read from the first
+// active lane so the descriptor lives in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0, n, 0x00020000);
 }
 __device__ __forceinline__ bf16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));

@@ -22,14 +22,15 @@ struct AttnPlan {
 
 constexpr int kQBlock = 128;      // queries per attention workgroup
 constexpr int kKeyTile = 64;      // keys per LDS tile
+constexpr int kMaxSplit = 8;      // most key ranges one attention call is cut into
 constexpr int kInterKeys = 128;   // keys the first range gives up for the inter-frame read
 constexpr int kDeltaChunk = 128;  // tokens per delta-update workgroup (MFMA path)
 constexpr int kGenChunk = 32;     // tokens per delta-update workgroup (generic path)
 
 AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk, bool inter);
 
-// Floats of partial output per (stream, head, query block, split): O[128][128]
-// and (max, sum)[128].
+// Elements of partial output per (stream, head, query block, split):
+// O/l[128][128] (bf16, in a slot sized for fp32) and (max, sum)[128] (fp32).
 constexpr int64_t kPartialO = 128 * 128;
 constexpr int64_t kPartialML = 128 * 2;
 

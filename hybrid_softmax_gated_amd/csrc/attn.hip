@@ -342,19 +342,21 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
     if (!step(std::integral_constant<int, 1>(), t0 + KB)) break;
   }
 
-  // Partial results in natural layout: O[query][d] (unnormalised), (m, l).
+  // Partial results: O / l of this key range in bf16, natural layout
+  // [query][d], and (m, l) in fp32 for the merge.
   const int64_t blk = (((int64_t)b * p.H + h) * p.nqblk + qblk) * p.nsplit + split;
-  float *wo = p.ws_o + blk * kPartialO + (wave * 32 + l32) * D;
+  const float lt = lsum + swap_halves(lsum);
+  const float il = 1.f / lt;
+  bf16 *wo = (bf16 *)p.ws_o + blk * kPartialO + (wave * 32 + l32) * D;
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      f32x4 t;
+      bf16x4 t;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = o[bb][4 * r + e];
-      *(f32x4 *)(wo + 32 * bb + 8 * r + 4 * hl) = t;
+      for (int e = 0; e < 4; ++e) t[e] = (bf16)(o[bb][4 * r + e] * il);
+      *(bf16x4 *)(wo + 32 * bb + 8 * r + 4 * hl) = t;
     }
-  const float lt = lsum + swap_halves(lsum);
   if (hl == 0) {
     float *wml = p.ws_ml + blk * kPartialML + 2 * (wave * 32 + l32);
     wml[0] = m;
@@ -368,9 +370,11 @@ struct MergeKParams {
   bf16 *out;
 };
 
-// out = (sum_s 2^(m_s - M) O_s) / (sum_s 2^(m_s - M) l_s) + O_inter, one
-// thread per (query, 4 consecutive head-dim values): a workgroup covers 8
-// queries of one query block, each row written as 256 contiguous bytes.
+// out = (sum_s w_s l_s Ohat_s) / (sum_s w_s l_s) + O_inter with
+// w_s = 2^(m_s - M) and Ohat_s = O_s / l_s the normalised partial of key
+// range s; one thread per (query, 4 consecutive head-dim values): a
+// workgroup covers 8 queries of one query block, each row written as 256
+// contiguous bytes.
 __global__ __launch_bounds__(256) void merge_kernel(MergeKParams p) {
   const int grp = blockIdx.x & 15;   // 8-query group within the 128-query block
   const int blkq = blockIdx.x >> 4;  // (b, h, qblk)
@@ -381,22 +385,35 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeKParams p) {
   const int qrow = qblk * kQBlock + qi;
   if (qrow >= p.L) return;
   const int64_t blk0 = (int64_t)blkq * p.nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, p.ws_ml[(blk0 + s) * kPartialML + 2 * qi]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float Lt = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float *ml = p.ws_ml + (blk0 + s) * kPartialML + 2 * qi;
-    const float w = exp2_fast(ml[0] - M);
-    Lt = fmaf(w, ml[1], Lt);
-    const f32x4 v = *(const f32x4 *)(p.ws_o + (blk0 + s) * kPartialO + qi * D + 4 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, v[e], acc[e]);
-  }
-  const float inv = 1.f / Lt;
+  // Issue every load of this thread before using any of them.
   f32x4 add = {0.f, 0.f, 0.f, 0.f};
   if (p.ws_inter)
     add = *(const f32x4 *)(p.ws_inter + ((int64_t)bh * p.nqblk * kQBlock + qrow) * D + 4 * c);
+  float mv[kMaxSplit], lv[kMaxSplit];
+  bf16x4 ov[kMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < p.nsplit) {
+      const float *ml = p.ws_ml + (blk0 + s) * kPartialML + 2 * qi;
+      mv[s] = ml[0];
+      lv[s] = ml[1];
+      ov[s] = *(const bf16x4 *)((const bf16 *)p.ws_o + (blk0 + s) * kPartialO + qi * D + 4 * c);
+    }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < p.nsplit) M = fmaxf(M, mv[s]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float Lt = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < p.nsplit) {
+      const float w = exp2_fast(mv[s] - M) * lv[s];
+      Lt += w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, (float)ov[s][e], acc[e]);
+    }
+  const float inv = 1.f / Lt;
   bf16x4 t;
 #pragma unroll
   for (int e = 0; e < 4; ++e) t[e] = (bf16)fmaf(acc[e], inv, add[e]);
@@ -414,7 +431,7 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk, bool inter
   int64_t ns = 512 / base;
   const int64_t max_by_keys = (Lk + 2 * kKeyTile - 1) / (2 * kKeyTile);
   if (ns > max_by_keys) ns = max_by_keys;
-  if (ns > 16) ns = 16;
+  if (ns > kMaxSplit) ns = kMaxSplit;
   if (ns < 1) ns = 1;
   // The first range is shorter by the inter-frame read's share of work.
   const int64_t shift = (inter && ns > 1) ? kInterKeys : 0;

@@ -17,7 +17,9 @@ cycled; everything is resident in HBM when the timed region starts.
 Prints one JSON line (the driver's contract) with, besides frames/s:
   roofline      the dominant kernel (intra-frame attention) against the bf16
                 dense MFMA peak, from its average launch duration measured
-                with HIP events on its launch stream (arl2_profile_*);
+                with HIP events on its launch stream (arl2_profile_*) in a
+                leg after the timed region, each idempotent kernel launched
+                --profile-repeat times back to back per event pair;
   cpu_baseline  the float64 oracle on this host's cores, on a bounded sample.
 """
 from __future__ import annotations
@@ -68,7 +70,7 @@ def measured_traffic(kernel, workload, digest):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(frames_host, W, w, budget_s=12.0, max_frames=24):
+def cpu_baseline(frames_host, W, w, budget_s=15.0, max_frames=400):
     """Time the float64 oracle on host copies of the same frames."""
     import numpy as np
     import oracle as O
@@ -98,7 +100,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="frame_step_480p",
                     choices=["frame_step_480p", "stream21_480p", "batched720p"])
-    ap.add_argument("--profile-steps", type=int, default=300)
+    ap.add_argument("--profile-steps", type=int, default=100)
+    ap.add_argument("--profile-repeat", type=int, default=10,
+                    help="back-to-back launches of each idempotent kernel per event pair "
+                         "in the per-kernel timing leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB 10 times (scales the HBM byte "
@@ -172,7 +177,7 @@ def main() -> int:
 
     # ---- per-kernel durations with HIP events on the launch stream
     Bd.arl2_profile_reset()
-    Bd.arl2_profile_enable(True)
+    Bd.arl2_profile_enable(True, args.profile_repeat)
     for i in range(args.profile_steps):
         step(i)
     torch.cuda.synchronize()

@@ -68,7 +68,7 @@ def _load() -> ctypes.CDLL:
         "arl2_frame_forward": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, P, P, I, P]),
         "arl2_softmax_attention_workspace_bytes": (Z, [I, I, I, I, I, I]),
         "arl2_softmax_attention": (I, [P, P, P, I, I, I, I, I, I, P, P, Z, P]),
-        "arl2_profile_enable": (I, [I]),
+        "arl2_profile_enable": (I, [I, I]),
         "arl2_profile_report": (I, [ctypes.c_char_p, Z]),
         "arl2_profile_reset": (None, []),
     }
@@ -156,8 +156,8 @@ def arl2_softmax_attention(q, kc, vc, B: int, H: int, d: int, Lq: int, Lk: int, 
                                        _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def arl2_profile_enable(on: bool) -> None:
-    _check(_lib.arl2_profile_enable(1 if on else 0))
+def arl2_profile_enable(on: bool, repeat: int = 1) -> None:
+    _check(_lib.arl2_profile_enable(1 if on else 0, int(repeat)))
 
 
 def arl2_profile_reset() -> None:

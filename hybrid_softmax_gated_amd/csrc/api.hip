@@ -139,7 +139,9 @@ AttnOnlyPlan plan_attn_only(int64_t B, int64_t H, int64_t d, int64_t Lq, int64_t
 struct Profiler {
   std::mutex mu;
   bool on = false;
+  int repeat = 1;  // launches of an idempotent kernel between one event pair
   struct Rec {
+    int count;
     size_t kernel;
     hipEvent_t a, b;
   };
@@ -173,7 +175,7 @@ struct Profiler {
       hipError_t e = hipEventSynchronize(r.b);
       if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
       if (e == hipSuccess) {
-        launches[r.kernel] += 1;
+        launches[r.kernel] += r.count;
         total_ms[r.kernel] += ms;
       } else if (err == hipSuccess) {
         err = e;
@@ -191,9 +193,12 @@ Profiler &profiler() {
   return p;
 }
 
-// Launch through `fn`, bracketed by timing events when profiling is on.
+// Launch through `fn`, bracketed by timing events when profiling is on. A
+// kernel that only reads its inputs and overwrites its outputs (idempotent)
+// is launched `repeat` times back to back between the two events, so that
+// the events' own overhead is spread over the launches.
 template <class F>
-hipError_t timed(const char *name, hipStream_t s, F fn) {
+hipError_t timed(const char *name, hipStream_t s, F fn, bool idempotent = true) {
   Profiler &p = profiler();
   std::unique_lock<std::mutex> lk(p.mu);
   if (!p.on) {
@@ -204,10 +209,12 @@ hipError_t timed(const char *name, hipStream_t s, F fn) {
   hipError_t e = p.event(&a);
   if (e != hipSuccess) return e;
   if ((e = p.event(&b)) != hipSuccess) return e;
+  const int count = idempotent ? p.repeat : 1;
   if ((e = hipEventRecord(a, s)) != hipSuccess) return e;
-  if ((e = fn()) != hipSuccess) return e;
+  for (int i = 0; i < count; ++i)
+    if ((e = fn()) != hipSuccess) return e;
   if ((e = hipEventRecord(b, s)) != hipSuccess) return e;
-  p.pending.push_back({p.id(name), a, b});
+  p.pending.push_back({count, p.id(name), a, b});
   return hipSuccess;
 }
 
@@ -392,7 +399,7 @@ arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, cons
   if (update_flag) {
     if ((e = timed("delta_apply", s, [&] {
            return arl2::launch_delta_apply(S, alpha, ws_ds, iB, iH, id, fp.nchunk, s);
-         })))
+         }, /*idempotent=*/false)))
       return hip_status(e, fn);
   }
   return ok();
@@ -463,10 +470,13 @@ arl2_status arl2_softmax_attention(const void *q, const void *kc, const void *vc
   return ok();
 }
 
-arl2_status arl2_profile_enable(int32_t on) {
+arl2_status arl2_profile_enable(int32_t on, int32_t repeat) {
+  if (repeat < 1 || repeat > 1000)
+    return fail(ARL2_ERR_INVALID_ARG, "arl2_profile_enable: repeat %d not in [1, 1000]", repeat);
   Profiler &p = profiler();
   std::lock_guard<std::mutex> lk(p.mu);
   p.on = on != 0;
+  p.repeat = repeat;
   return ok();
 }
 

@@ -158,15 +158,19 @@ ARL2_API arl2_status arl2_softmax_attention(const void *q, const void *kc, const
 
 /*
  * Kernel timing (diagnostics). While enabled, every kernel the library
- * launches is bracketed by a pair of hipEvents recorded on the launch stream;
- * arl2_profile_report waits for the recorded events and writes one line per
- * kernel, "<name> <launches> <total_ms>\n", into buf (NUL-terminated,
- * truncated to len). Disabled by default; event records add a small gap
- * between launches while enabled. Not for use under graph capture.
- * Errors: INVALID_ARG for a NULL buf or len 0; ARL2_ERR_HIP if an event
- * cannot be created or queried.
+ * launches is bracketed by a pair of hipEvents recorded on the launch stream.
+ * A kernel that only reads its inputs and overwrites its outputs (all but
+ * the in-place state update) is launched `repeat` times back to back inside
+ * its pair, which spreads the events' own overhead over `repeat` launches;
+ * the results are those of a single launch. repeat = 1 launches every kernel
+ * once. arl2_profile_report waits for the recorded events and writes one
+ * line per kernel, "<name> <launches> <total_ms>\n", into buf
+ * (NUL-terminated, truncated to len). Disabled by default. Not for use under
+ * graph capture.
+ * Errors: INVALID_ARG for repeat outside [1, 1000], a NULL buf or len 0;
+ * ARL2_ERR_HIP if an event cannot be created or queried.
  */
-ARL2_API arl2_status arl2_profile_enable(int32_t on);
+ARL2_API arl2_status arl2_profile_enable(int32_t on, int32_t repeat);
 ARL2_API arl2_status arl2_profile_report(char *buf, size_t len);
 ARL2_API void arl2_profile_reset(void);
 

@@ -49,6 +49,10 @@ def test_profile_report_without_launches(B):
     B.arl2_profile_reset()
     assert B.arl2_profile_report() == {}
     B.arl2_profile_enable(False)
+    for bad in (0, -1, 1001):
+        with pytest.raises(B.ARL2Error, match="repeat"):
+            B.arl2_profile_enable(True, bad)
+    B.arl2_profile_enable(False, 1)
 
 
 def test_version_and_status_strings(B):

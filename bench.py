@@ -191,7 +191,7 @@ def main() -> int:
     tflops = frame_flops * fps / 1e12
     att_s = kern_us["attn_partial"] * 1e-6
     att_tflops = fa / att_s / 1e12
-    digest = source_digest("attn.hip", "arl2_device.h", "mfma_stage.h")
+    digest = source_digest("attn.hip", "arl2_device.h")
     roofline = {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic("attn_partial", args.workload, digest),

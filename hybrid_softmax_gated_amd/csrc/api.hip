@@ -82,19 +82,18 @@ struct FramePlan {
   bool mfma = false;
   arl2::AttnPlan ap;
   int nchunk = 0;
-  size_t off_o = 0, off_ml = 0, off_inter = 0, off_ds = 0, total = 0;
+  size_t off_o = 0, off_ml = 0, off_ds = 0, total = 0;
 };
 
 FramePlan plan_frame(int64_t B, int64_t H, int64_t d, int64_t L, int32_t dtype) {
   FramePlan fp;
   fp.mfma = mfma_path((int32_t)d, dtype);
-  size_t o_bytes, ml_bytes, inter_bytes = 0;
+  size_t o_bytes, ml_bytes;
   if (fp.mfma) {
-    fp.ap = arl2::plan_attention(B, H, L, L, true);
+    fp.ap = arl2::plan_attention(B, H, L, L);
     const size_t blocks = (size_t)B * H * fp.ap.nqblk * fp.ap.nsplit;
-    o_bytes = blocks * arl2::kPartialO * sizeof(float);
+    o_bytes = blocks * arl2::kPartialOBytes;
     ml_bytes = blocks * arl2::kPartialML * sizeof(float);
-    inter_bytes = (size_t)B * H * fp.ap.nqblk * arl2::kQBlock * d * sizeof(float);
     fp.nchunk = (int)((L + arl2::kDeltaChunk - 1) / arl2::kDeltaChunk);
   } else {
     o_bytes = (size_t)B * H * L * d * sizeof(float);
@@ -104,8 +103,7 @@ FramePlan plan_frame(int64_t B, int64_t H, int64_t d, int64_t L, int32_t dtype) 
   const size_t ds_bytes = (size_t)B * H * fp.nchunk * d * d * sizeof(float);
   fp.off_o = 0;
   fp.off_ml = align256(o_bytes);
-  fp.off_inter = fp.off_ml + align256(ml_bytes);
-  fp.off_ds = fp.off_inter + align256(inter_bytes);
+  fp.off_ds = fp.off_ml + align256(ml_bytes);
   fp.total = fp.off_ds + align256(ds_bytes);
   return fp;
 }
@@ -122,9 +120,9 @@ AttnOnlyPlan plan_attn_only(int64_t B, int64_t H, int64_t d, int64_t Lq, int64_t
   p.mfma = mfma_path((int32_t)d, dtype);
   size_t o_bytes, ml_bytes = 0;
   if (p.mfma) {
-    p.ap = arl2::plan_attention(B, H, Lq, Lk, false);
+    p.ap = arl2::plan_attention(B, H, Lq, Lk);
     const size_t blocks = (size_t)B * H * p.ap.nqblk * p.ap.nsplit;
-    o_bytes = blocks * arl2::kPartialO * sizeof(float);
+    o_bytes = blocks * arl2::kPartialOBytes;
     ml_bytes = blocks * arl2::kPartialML * sizeof(float);
   } else {
     o_bytes = (size_t)B * H * Lq * d * sizeof(float);
@@ -356,7 +354,6 @@ arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, cons
   char *ws = (char *)st->ws;
   float *ws_o = (float *)(ws + fp.off_o);
   float *ws_ml = (float *)(ws + fp.off_ml);
-  float *ws_inter = (float *)(ws + fp.off_inter);
   float *ws_ds = (float *)(ws + fp.off_ds);
   const char *wbase = (const char *)Wphi;
   const void *Wq = wbase;
@@ -367,17 +364,15 @@ arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, cons
   float *S = st->S;
   hipError_t e;
   if (fp.mfma) {
-    const arl2::AttnArgs aa{q, k, v, Wq, S, iB, iH, iL, iL, fp.ap, ws_o, ws_ml, ws_inter};
-    const arl2::MergeArgs ma{ws_o, ws_ml, ws_inter, iB, iH, iL, fp.ap, out};
+    const arl2::AttnArgs aa{q, k, v, iB, iH, iL, iL, fp.ap, ws_o, ws_ml};
+    const arl2::CombineArgs ca{ws_o, ws_ml, q, Wq, S, iB, iH, iL, fp.ap, out};
+    const arl2::DeltaArgs da{k, v, Wk, Wv, S, beta, iB, iH, iL, fp.nchunk, ws_ds};
     if ((e = timed("attn_partial", s, [&] { return arl2::launch_attn_partial_bf16(aa, s); })))
       return hip_status(e, fn);
-    if ((e = timed("merge", s, [&] { return arl2::launch_merge_bf16(ma, s); })))
+    if ((e = timed(update_flag ? "combine_delta" : "combine", s, [&] {
+           return arl2::launch_tail_bf16(ca, update_flag ? &da : nullptr, s);
+         })))
       return hip_status(e, fn);
-    if (update_flag) {
-      const arl2::DeltaArgs da{k, v, Wk, Wv, S, beta, iB, iH, iL, fp.nchunk, ws_ds};
-      if ((e = timed("delta_partial", s, [&] { return arl2::launch_delta_partial_bf16(da, s); })))
-        return hip_status(e, fn);
-    }
   } else {
     if ((e = timed("generic_attention", s, [&] {
            return arl2::launch_generic_attention(dt, id, q, k, v, iB, iH, iL, iL, ws_o, s);
@@ -450,11 +445,11 @@ arl2_status arl2_softmax_attention(const void *q, const void *kc, const void *vc
   float *ws_ml = (float *)((char *)ws + ap.off_ml);
   hipError_t e;
   if (ap.mfma) {
-    const arl2::AttnArgs aa{q, kc, vc, nullptr, nullptr, B, H, Lq, Lk, ap.ap, ws_o, ws_ml, nullptr};
-    const arl2::MergeArgs ma{ws_o, ws_ml, nullptr, B, H, Lq, ap.ap, out};
+    const arl2::AttnArgs aa{q, kc, vc, B, H, Lq, Lk, ap.ap, ws_o, ws_ml};
+    const arl2::CombineArgs ca{ws_o, ws_ml, q, nullptr, nullptr, B, H, Lq, ap.ap, out};
     if ((e = timed("attn_partial", s, [&] { return arl2::launch_attn_partial_bf16(aa, s); })))
       return hip_status(e, fn);
-    if ((e = timed("merge", s, [&] { return arl2::launch_merge_bf16(ma, s); })))
+    if ((e = timed("combine", s, [&] { return arl2::launch_tail_bf16(ca, nullptr, s); })))
       return hip_status(e, fn);
   } else {
     if ((e = timed("generic_attention", s, [&] {

@@ -95,6 +95,21 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void *lds_byte_addr) {
       (__attribute__((address_space(3))) s16x4 *)(lds_byte_addr));
 }
 
+// MFMA operand read transposed from a swizzled row-major 128-column bf16
+// tile (tile_off): lane l gets column 32bb + l%32 of the tile, rows k0 ..
+// k0+3 in elements 0..3 and rows k1 .. k1+3 in elements 4..7 (k0 and k1
+// may differ between the wave halves). A and B operands share this
+// register layout, so the result serves as either.
+__device__ __forceinline__ bf16x8 tile_col_operand(const char *tile, int k0, int k1, int lane,
+                                                   int bb) {
+  const int gi = lane & 15, g = lane >> 4;
+  const int col = 32 * bb + 16 * (g & 1) + 4 * (gi & 3);
+  const s16x4 lo = lds_read_tr16(tile + tile_off(k0 + (gi >> 2), col >> 3) + 2 * (col & 7));
+  const s16x4 hi = lds_read_tr16(tile + tile_off(k1 + (gi >> 2), col >> 3) + 2 * (col & 7));
+  return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                        lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane i's 16 bytes land at
 // lds_base + 16 * i (lds_base must be uniform across the wavefront).
 __device__ __forceinline__ void global_to_lds16(const void *gsrc, void *lds_base) {

@@ -12,7 +12,7 @@ namespace arl2 {
 // How one attention call is cut into workgroups: query blocks of 128 rows
 // (4 wavefronts x 32 queries) and `nsplit` contiguous key ranges: the first
 // holds `kps0` keys, the others `keys_per_split` (multiples of the 64-key
-// tile). Partial results of the key ranges are merged by the merge kernel.
+// tile). Partial results of the key ranges are merged by the combine kernel.
 struct AttnPlan {
   int nqblk = 0;
   int nsplit = 0;
@@ -23,38 +23,42 @@ struct AttnPlan {
 constexpr int kQBlock = 128;      // queries per attention workgroup
 constexpr int kKeyTile = 64;      // keys per LDS tile
 constexpr int kMaxSplit = 8;      // most key ranges one attention call is cut into
-constexpr int kInterKeys = 128;   // keys the first range gives up for the inter-frame read
 constexpr int kDeltaChunk = 128;  // tokens per delta-update workgroup (MFMA path)
 constexpr int kGenChunk = 32;     // tokens per delta-update workgroup (generic path)
 
-AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk, bool inter);
+AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk);
 
-// Elements of partial output per (stream, head, query block, split):
-// O/l[128][128] (bf16, in a slot sized for fp32) and (max, sum)[128] (fp32).
-constexpr int64_t kPartialO = 128 * 128;
+// Partial output per (stream, head, query block, split): O/l for 128
+// queries x 128 values in bf16 (in the attention accumulators' register
+// order), and (max, sum) per query in fp32.
+constexpr int64_t kPartialOBytes = 128 * 128 * 2;
 constexpr int64_t kPartialML = 128 * 2;
 
 // ---------------------------------------------------------------- MFMA path
 // bf16 io, d = 128.
 struct AttnArgs {
   const void *q, *k, *v;  // [B][Lq][H][128], [B][Lk][H][128]
-  const void *Wq;         // [H][128][128] (read when ws_inter is set)
-  const float *S;         // [B][H][128][128] (read when ws_inter is set)
   int B, H, Lq, Lk;
   AttnPlan plan;
-  float *ws_o, *ws_ml;
-  float *ws_inter;        // [B][H][nqblk*128][128] O_inter, or null for plain attention
+  void *ws_o;             // plan blocks x kPartialOBytes
+  float *ws_ml;           // plan blocks x kPartialML
 };
 hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s);
 
-struct MergeArgs {
-  const float *ws_o, *ws_ml, *ws_inter;  // ws_inter may be null
+// out = merged attention partials + L2norm(q W_q) S (the inter-frame read),
+// or the merged partials alone when Wq is null.
+struct CombineArgs {
+  const void *ws_o;
+  const float *ws_ml;
+  const void *q;   // [B][L][H][128]
+  const void *Wq;  // [H][128][128], or null
+  const float *S;  // [B][H][128][128] (read when Wq is set)
   int B, H, L;
   AttnPlan plan;
   void *out;  // [B][L][H][128] bf16
 };
-hipError_t launch_merge_bf16(const MergeArgs &a, hipStream_t s);
 
+// Chunk contributions dS_c of the gated delta update (clean pass).
 struct DeltaArgs {
   const void *k, *v;     // [B][L][H][128]
   const void *Wk, *Wv;   // [H][128][128]
@@ -63,7 +67,10 @@ struct DeltaArgs {
   int B, H, L, nchunk;
   float *ws_dS;          // [B][H][nchunk][128][128]
 };
-hipError_t launch_delta_partial_bf16(const DeltaArgs &a, hipStream_t s);
+
+// One launch for the combine and, when `d` is not null, the delta chunks:
+// both only read S, so they run side by side.
+hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_t s);
 
 // ---------------------------------------------------------------- shared
 // S[b][h] := alpha[b][h] * S[b][h] + sum over chunks c (in order) of

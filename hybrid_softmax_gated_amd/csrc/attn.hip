@@ -1,6 +1,6 @@
 // Intra-frame softmax attention (bf16, d = 128) on the gfx950 matrix cores,
-// and the epilogue that merges its key-range partials, adds the inter-frame
-// read O_inter = Q' S and writes the layer output.
+// and the combine kernel that merges its key-range partials with the
+// inter-frame read O_inter = Q' S and writes the layer output.
 //
 // Method: "Technical Summary: Attend Locally, Remember Linearly (ARL2)",
 // section 2.1 — the intra-frame branch keeps full bidirectional softmax
@@ -27,12 +27,14 @@
 //    the current tile's MFMAs and written to LDS after them (one barrier per
 //    tile); the loop is unrolled by two so every LDS address is a constant
 //    offset from a per-lane register;
-//  * the workgroups of the first key range also compute the inter-frame
-//    read O_inter = L2norm(q W_q) S_{N-1} for their queries before their key
-//    loop (that range is shorter by the equivalent work);
-//  * the unnormalised O, the row max (log2 domain) and the row sum are
-//    written per key range; a streaming kernel merges the ranges, adds
-//    O_inter and writes the output.
+//  * per key range it writes O/l in bf16, in the accumulators' register
+//    order (16-byte coalesced stores), and the row max (log2 domain) and row
+//    sum in fp32.
+//
+// Combine kernel (one workgroup = 128 queries of one head): the inter-frame
+// read (q W_q, L2 norms, Q' S on the matrix cores, with W_q and bf16(S) in
+// LDS), the merge of the key ranges in fp32, the sum of the two branches,
+// and the bf16 output rows, transposed through LDS into 256-byte stores.
 #include "arl2_device.h"
 #include "arl2_kernels.h"
 
@@ -48,12 +50,12 @@ constexpr int KB = kKeyTile;         // 64 keys per LDS tile
 constexpr int TILE_BYTES = KB * D * 2;  // 16 KB
 
 struct AttnKParams {
-  const bf16 *q, *k, *v, *Wq;
-  const float *S;
+  const bf16 *q, *k, *v;
   int H, Lq, Lk, nsplit, kps0, kps, nqblk;
   int nitems, per_xcd;  // work items and items per XCD (see item_of)
-  float *ws_o, *ws_ml, *ws_inter;  // ws_inter null: no inter-frame read
-  float scale;                     // log2(e) / sqrt(d)
+  char *ws_o;           // O/l partials, kPartialOBytes per block
+  float *ws_ml;         // (max, sum) per query, kPartialML floats per block
+  float scale;          // log2(e) / sqrt(d)
 };
 
 // Work items are (stream, head, split, query block) with the query block
@@ -63,61 +65,6 @@ struct AttnKParams {
 // that XCD's L2.
 __device__ __forceinline__ int item_of(int bid, int per_xcd) {
   return (bid & 7) * per_xcd + (bid >> 3);
-}
-
-// A operand (rows = 32 columns 32bb .. 32bb+31 of the tile, k = 8 tile
-// rows) read transposed from a swizzled row-major 128-column bf16 tile: rows
-// k0 .. k0+3 land in elements 0..3 and rows k1 .. k1+3 in elements 4..7.
-__device__ __forceinline__ bf16x8 tile_col_operand(const char *tile, int k0, int k1, int lane,
-                                                   int bb) {
-  const int gi = lane & 15, g = lane >> 4;
-  const int col = 32 * bb + 16 * (g & 1) + 4 * (gi & 3);
-  const s16x4 lo = lds_read_tr16(tile + tile_off(k0 + (gi >> 2), col >> 3) + 2 * (col & 7));
-  const s16x4 hi = lds_read_tr16(tile + tile_off(k1 + (gi >> 2), col >> 3) + 2 * (col & 7));
-  return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
-                                        lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-}
-
-// O_inter for the wavefront's 32 queries (lane = query, registers = d_v),
-// from W_q[h] (rows 0..63 in W0, 64..127 in W1) and bf16(S) (rows 0..63 in
-// S0, 64..127 in S1), each half a swizzled 64-row tile in LDS:
-// (q W_q)^T = W_q^T q^T, Q' = its columns scaled to unit length, then
-// O_inter^T = S^T Q'^T with Q' fed straight from the accumulators: register
-// 8*(g%2) + j of block g/2 holds feature 16g + swap_bits23(8*(l/32) + j),
-// i.e. rows 16g + 4*(l/32) + {0..3} and 16g + 8 + 4*(l/32) + {0..3} of S.
-__device__ __forceinline__ void inter_read_wave(const char *W0, const char *W1, const char *S0,
-                                                const char *S1, const bf16x8 (&qop)[8], int lane,
-                                                f32x16 (&oi)[4]) {
-  const int hl = lane >> 5;
-  f32x16 qp4[4];
-#pragma unroll
-  for (int bb = 0; bb < 4; ++bb) {
-    qp4[bb] = zero16();
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int k0 = (16 * c + 8 * hl) & 63;
-      qp4[bb] = mfma32(tile_col_operand(c < 4 ? W0 : W1, k0, k0 + 4, lane, bb), qop[c], qp4[bb]);
-    }
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ss = fmaf(qp4[bb][i], qp4[bb][i], ss);
-  ss += swap_halves(ss);
-  const float inv = 1.f / fmaxf(sqrtf(ss), kL2Eps);
-#pragma unroll
-  for (int bb = 0; bb < 4; ++bb) oi[bb] = zero16();
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    bf16x8 qb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qb[j] = (bf16)(qp4[g >> 1][8 * (g & 1) + j] * inv);
-    const int k0 = (16 * g + 4 * hl) & 63;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-      oi[bb] = mfma32(tile_col_operand(g < 4 ? S0 : S1, k0, k0 + 8, lane, bb), qb, oi[bb]);
-  }
 }
 
 __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
@@ -180,49 +127,6 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
   } else {
 #pragma unroll
     for (int c = 0; c < 8; ++c) qop[c] = zero_bf16x8();
-  }
-
-  if (split == 0 && p.ws_inter) {
-    // W_q[h] rows 0..63 in Ks0, 64..127 in Ks1 (copied straight into LDS);
-    // bf16(S[b][h]) rows 0..63 in Vs0, 64..127 in Vs1.
-    const bf16 *W = p.Wq + (int64_t)h * D * D;
-    const int r4 = lane >> 4, pos = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int cc = 8 * wave + i, row = 4 * cc + r4;
-      global_to_lds16(W + row * D + 8 * (pos ^ tile_swz(row & 15)),
-                      (cc < 16 ? Ks0 : Ks1) + (cc & 15) * 1024);
-    }
-    const float *Sh = p.S + ((int64_t)b * p.H + h) * D * D;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 4) + 16 * i, u = tid & 15;
-      const f32x4 a = *(const f32x4 *)(Sh + row * D + 8 * u);
-      const f32x4 c = *(const f32x4 *)(Sh + row * D + 8 * u + 4);
-      bf16x8 t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t[e] = (bf16)a[e];
-        t[4 + e] = (bf16)c[e];
-      }
-      *(bf16x8 *)((i < 4 ? Vs0 : Vs1) + tile_off(row & 63, u)) = t;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    f32x16 oi[4];
-    inter_read_wave(Ks0, Ks1, Vs0, Vs1, qop, lane, oi);
-    float *dst = p.ws_inter + (((int64_t)b * p.H + h) * p.nqblk * kQBlock + qblk * kQBlock +
-                               wave * 32 + l32) * D;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        f32x4 t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = oi[bb][4 * r + e];
-        *(f32x4 *)(dst + 32 * bb + 8 * r + 4 * hl) = t;
-      }
-    __syncthreads();  // LDS is free for the key tiles
   }
 
   copy_tile(kbeg, Ks0, Vs0);
@@ -342,20 +246,22 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
     if (!step(std::integral_constant<int, 1>(), t0 + KB)) break;
   }
 
-  // Partial results: O / l of this key range in bf16, natural layout
-  // [query][d], and (m, l) in fp32 for the merge.
+  // Partial results: O / l of this key range in bf16, in register order
+  // (one 16-byte unit per lane and (bb, r2): elements 4*(2*r2 + e2) + e of
+  // o[bb], i.e. d_v = 32bb + 16*r2 + 8*e2 + 4*(l/32) + e), and (m, l) in
+  // fp32 per query for the merge.
   const int64_t blk = (((int64_t)b * p.H + h) * p.nqblk + qblk) * p.nsplit + split;
   const float lt = lsum + swap_halves(lsum);
   const float il = 1.f / lt;
-  bf16 *wo = (bf16 *)p.ws_o + blk * kPartialO + (wave * 32 + l32) * D;
+  char *wo = p.ws_o + blk * kPartialOBytes + (wave * 8 * 64 + lane) * 16;
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      bf16x4 t;
+    for (int r2 = 0; r2 < 2; ++r2) {
+      bf16x8 t;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = (bf16)(o[bb][4 * r + e] * il);
-      *(bf16x4 *)(wo + 32 * bb + 8 * r + 4 * hl) = t;
+      for (int e = 0; e < 8; ++e) t[e] = (bf16)(o[bb][8 * r2 + e] * il);
+      *(bf16x8 *)(wo + (2 * bb + r2) * 64 * 16) = t;
     }
   if (hl == 0) {
     float *wml = p.ws_ml + blk * kPartialML + 2 * (wave * 32 + l32);
@@ -364,65 +270,9 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
   }
 }
 
-struct MergeKParams {
-  const float *ws_o, *ws_ml, *ws_inter;  // ws_inter may be null
-  int H, L, nqblk, nsplit;
-  bf16 *out;
-};
-
-// out = (sum_s w_s l_s Ohat_s) / (sum_s w_s l_s) + O_inter with
-// w_s = 2^(m_s - M) and Ohat_s = O_s / l_s the normalised partial of key
-// range s; one thread per (query, 4 consecutive head-dim values): a
-// workgroup covers 8 queries of one query block, each row written as 256
-// contiguous bytes.
-__global__ __launch_bounds__(256) void merge_kernel(MergeKParams p) {
-  const int grp = blockIdx.x & 15;   // 8-query group within the 128-query block
-  const int blkq = blockIdx.x >> 4;  // (b, h, qblk)
-  const int qi = grp * 8 + (threadIdx.x >> 5), c = threadIdx.x & 31;
-  const int qblk = blkq % p.nqblk;
-  const int bh = blkq / p.nqblk;
-  const int h = bh % p.H, b = bh / p.H;
-  const int qrow = qblk * kQBlock + qi;
-  if (qrow >= p.L) return;
-  const int64_t blk0 = (int64_t)blkq * p.nsplit;
-  // Issue every load of this thread before using any of them.
-  f32x4 add = {0.f, 0.f, 0.f, 0.f};
-  if (p.ws_inter)
-    add = *(const f32x4 *)(p.ws_inter + ((int64_t)bh * p.nqblk * kQBlock + qrow) * D + 4 * c);
-  float mv[kMaxSplit], lv[kMaxSplit];
-  bf16x4 ov[kMaxSplit];
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s)
-    if (s < p.nsplit) {
-      const float *ml = p.ws_ml + (blk0 + s) * kPartialML + 2 * qi;
-      mv[s] = ml[0];
-      lv[s] = ml[1];
-      ov[s] = *(const bf16x4 *)((const bf16 *)p.ws_o + (blk0 + s) * kPartialO + qi * D + 4 * c);
-    }
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s)
-    if (s < p.nsplit) M = fmaxf(M, mv[s]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float Lt = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s)
-    if (s < p.nsplit) {
-      const float w = exp2_fast(mv[s] - M) * lv[s];
-      Lt += w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, (float)ov[s][e], acc[e]);
-    }
-  const float inv = 1.f / Lt;
-  bf16x4 t;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) t[e] = (bf16)fmaf(acc[e], inv, add[e]);
-  *(bf16x4 *)(p.out + (((int64_t)b * p.L + qrow) * p.H + h) * D + 4 * c) = t;
-}
-
 }  // namespace
 
-AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk, bool inter) {
+AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
   AttnPlan pl;
   pl.nqblk = (int)((Lq + kQBlock - 1) / kQBlock);
   const int64_t base = B * H * pl.nqblk;
@@ -433,15 +283,11 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk, bool inter
   if (ns > max_by_keys) ns = max_by_keys;
   if (ns > kMaxSplit) ns = kMaxSplit;
   if (ns < 1) ns = 1;
-  // The first range is shorter by the inter-frame read's share of work.
-  const int64_t shift = (inter && ns > 1) ? kInterKeys : 0;
-  int64_t kps = (Lk + shift + ns - 1) / ns;
+  int64_t kps = (Lk + ns - 1) / ns;
   kps = (kps + kKeyTile - 1) / kKeyTile * kKeyTile;
-  int64_t kps0 = kps - shift;
-  if (kps0 < kKeyTile) kps0 = kKeyTile;
-  pl.kps0 = (int)kps0;
+  pl.kps0 = (int)kps;
   pl.keys_per_split = (int)kps;
-  pl.nsplit = Lk <= kps0 ? 1 : (int)(1 + (Lk - kps0 + kps - 1) / kps);
+  pl.nsplit = (int)((Lk + kps - 1) / kps);
   return pl;
 }
 
@@ -450,8 +296,6 @@ hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s) {
   p.q = (const bf16 *)a.q;
   p.k = (const bf16 *)a.k;
   p.v = (const bf16 *)a.v;
-  p.Wq = (const bf16 *)a.Wq;
-  p.S = a.S;
   p.H = a.H;
   p.Lq = a.Lq;
   p.Lk = a.Lk;
@@ -459,28 +303,12 @@ hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s) {
   p.kps0 = a.plan.kps0;
   p.kps = a.plan.keys_per_split;
   p.nqblk = a.plan.nqblk;
-  p.ws_o = a.ws_o;
+  p.ws_o = (char *)a.ws_o;
   p.ws_ml = a.ws_ml;
-  p.ws_inter = a.ws_inter;
   p.scale = kLog2e / sqrtf((float)D);
   p.nitems = a.B * a.H * a.plan.nsplit * a.plan.nqblk;
   p.per_xcd = (p.nitems + 7) / 8;
   hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)(8 * p.per_xcd)), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_merge_bf16(const MergeArgs &a, hipStream_t s) {
-  MergeKParams p;
-  p.ws_o = a.ws_o;
-  p.ws_ml = a.ws_ml;
-  p.ws_inter = a.ws_inter;
-  p.H = a.H;
-  p.L = a.L;
-  p.nqblk = a.plan.nqblk;
-  p.nsplit = a.plan.nsplit;
-  p.out = (bf16 *)a.out;
-  const int64_t blocks = (int64_t)a.B * a.H * a.plan.nqblk * 16;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,197 @@
+"""The streaming workloads at full size on the GPU against the float64 oracle.
+
+Inputs are drawn on the GPU (synth_inputs.iter_passes_device) and the exact
+bytes are copied back for the oracle. The oracle carries its own state from
+frame to frame and is never re-synced to the GPU's.
+
+Per clean pass the whole state is compared (max-norm relative error per
+(stream, head) <= 1e-3). Outputs are compared on sampled rows (first and
+last rows, tile edges, random rows) of every (stream, head), computed by the
+oracle one row at a time (<= 2e-2 for bf16 io).
+
+The literal update is expansive at the 480p shape (the frame transition has
+spectral radius about 10), so the 231-frame literal run is compared on the
+frames before the oracle's state leaves the fp32 range, and the GPU state
+must turn non-finite within one frame of that point. The companion runs
+(beta / L) keep the state bounded and are compared on every frame.
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth_inputs as SI
+from parity_utils import (TOL_OUT, TOL_S, device, oracle_state_update, out_err_per_head,
+                          sample_rows, state_err, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+FP32_MAX = float(np.finfo(np.float32).max)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    device()
+    return t
+
+
+@pytest.fixture(scope="module")
+def lay(torch):
+    from hybrid_softmax_gated_amd import layer
+    return layer
+
+
+def _oracle_rows(q_rows, k, v, W, S):
+    """Oracle output of the sampled query rows q_rows [B][R][H][d] of every
+    (stream, head) over the whole frame k, v [B][L][H][d]."""
+    B, R, H, d = q_rows.shape
+    out = np.empty((B, R, H, d))
+    for b in range(B):
+        for h in range(H):
+            out[b, :, h] = O.output_rows(q_rows[b, :, h], k[b, :, h], v[b, :, h], W[0, h],
+                                         S[b, h], np.arange(R))
+    return out
+
+
+def _stream(lay, torch, w, frames=None, rows_n=12, out_every=1, until_overflow=False):
+    """Runs a workload; returns per-clean-pass records and the output errors.
+
+    out_every: compare sampled outputs on every pass (1) or on the first
+    query-only pass and the clean pass of every frame (0)."""
+    layer = lay.ARL2Layer(w.B, w.H, w.d, w.L, 0)
+    W = SI.make_weights(w)
+    Wd = to_dev(W, w.dtype)
+    S_ref = SI.make_state0(w).astype(np.float64)
+    if np.any(S_ref):
+        layer.reset(torch.from_numpy(S_ref.astype(np.float32)).to(device()))
+    out = torch.empty((w.B, w.L, w.H, w.d), dtype=SI.torch_dtype(w.dtype), device=device())
+    rows = sample_rows(w.L, rows_n, w.seed + 7)
+    rows_t = torch.from_numpy(rows).to(device())
+    recs, out_errs, mem = [], [], []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    frame_ms, t_frame = [], 0.0
+    for p in SI.iter_passes_device(w, device(), frames):
+        ref_finite = bool(np.max(np.abs(S_ref)) < FP32_MAX)
+        ev[0].record()
+        layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update)
+        ev[1].record()
+        torch.cuda.synchronize()
+        t_frame += ev[0].elapsed_time(ev[1])
+        check_out = ref_finite and (out_every == 1 or p.index == 0 or p.update)
+        if check_out or p.update:
+            k = p.k.float().cpu().numpy()
+            v = p.v.float().cpu().numpy()
+        if check_out:
+            q_rows = p.q.index_select(1, rows_t).float().cpu().numpy()
+            got = out.index_select(1, rows_t).float().cpu().numpy().astype(np.float64)
+            out_errs.append((p.frame, out_err_per_head(got, _oracle_rows(q_rows, k, v, W, S_ref))))
+        if p.update:
+            # the same tensors are alive at every clean pass: the library
+            # itself allocates nothing
+            mem.append(torch.cuda.memory_allocated())
+            frame_ms.append(t_frame)
+            t_frame = 0.0
+            oracle_state_update(S_ref, k, v, W, p.alpha.cpu().numpy(), p.beta.cpu().numpy())
+            S_gpu = to_host(layer.S)
+            rec = {"frame": p.frame, "ref_finite": bool(np.max(np.abs(S_ref)) < FP32_MAX),
+                   "gpu_finite": bool(np.all(np.isfinite(S_gpu))),
+                   "norm": float(np.max(np.abs(S_ref)))}
+            if rec["ref_finite"] and rec["gpu_finite"]:
+                rec["err"] = state_err(S_gpu, S_ref)
+            recs.append(rec)
+            if until_overflow and not rec["ref_finite"] and not rec["gpu_finite"]:
+                break
+    assert len(set(mem)) == 1, f"device memory changed across frames: {sorted(set(mem))}"
+    return recs, out_errs, frame_ms
+
+
+def _check(recs, out_errs, name, before_frame=None):
+    if before_frame is not None:
+        recs = [r for r in recs if r["frame"] < before_frame]
+        out_errs = [e for e in out_errs if e[0] < before_frame]
+    out_errs = [e for _, e in out_errs]
+    errs = [r["err"] for r in recs if "err" in r]
+    print(f"{name}: {len(recs)} clean passes, max S err {max(errs):.2e}, "
+          f"{len(out_errs)} passes with sampled outputs, max out err {max(out_errs):.2e}, "
+          f"final max|S| {recs[-1]['norm']:.3e}")
+    assert max(errs) < TOL_S
+    assert max(out_errs) < TOL_OUT[SI.BF16]
+
+
+@pytest.mark.parametrize("companion", [False, True])
+def test_stream21_480p(lay, torch, companion):
+    """21 latent frames, 4 query-only passes + 1 clean pass each, fresh
+    q, k, v every pass, state carried across frames from S0 = 0."""
+    w = SI.WORKLOADS["stream21_480p"]
+    w = SI.companion(w) if companion else w
+    recs, out_errs, _ = _stream(lay, torch, w)
+    assert len(recs) == 21 and all(r["gpu_finite"] and r["ref_finite"] for r in recs)
+    _check(recs, out_errs, w.name)
+
+
+def test_long231_480p_beta_over_L(lay, torch):
+    """231 frames (one query-only + one clean pass each) with the bounded
+    companion gates: the state is compared on every frame, device memory
+    stays constant, and the per-frame GPU time does not grow with the frame
+    index."""
+    w = SI.companion(SI.WORKLOADS["long231_480p"])
+    recs, out_errs, frame_ms = _stream(lay, torch, w, rows_n=8)
+    assert len(recs) == 231
+    _check(recs, out_errs, w.name)
+    first, last = np.median(frame_ms[5:35]), np.median(frame_ms[-30:])
+    print(f"GPU ms per frame: frames 6-35 median {first:.4f}, last 30 median {last:.4f}")
+    assert last < 1.5 * first
+
+
+def test_long231_480p_literal(lay, torch):
+    """The literal gates: compared frame by frame until the oracle's state
+    leaves the fp32 range; the GPU's state must turn non-finite within one
+    frame of that point (fp32 cannot hold it, the float64 oracle can)."""
+    w = SI.WORKLOADS["long231_480p"]
+    recs, out_errs, _ = _stream(lay, torch, w, rows_n=8, until_overflow=True)
+    first_ref = next((r["frame"] for r in recs if not r["ref_finite"]), None)
+    first_gpu = next((r["frame"] for r in recs if not r["gpu_finite"]), None)
+    print(f"oracle state leaves fp32 range at frame {first_ref}, GPU state non-finite at "
+          f"frame {first_gpu}")
+    assert first_ref is not None and first_gpu is not None
+    assert abs(first_gpu - first_ref) <= 1
+    _check(recs, out_errs, w.name, before_frame=min(first_ref, first_gpu))
+
+
+def test_batched720p(lay, torch):
+    """Four independent streams (seeds 0..3) at the 720p latent shape
+    (L = 3600), 21 frames of 4 query-only + 1 clean pass; sampled outputs
+    on every pass."""
+    w = SI.WORKLOADS["batched720p"]
+    t0 = time.time()
+    recs, out_errs, _ = _stream(lay, torch, w, rows_n=8)
+    print(f"batched720p took {time.time() - t0:.1f} s")
+    assert len(recs) == 21
+    _check(recs, out_errs, w.name)
+
+
+def test_kv_cache_attention_at_231_frames(lay, torch):
+    """The comparator at the long horizon's end: one frame's queries (12
+    heads, L = 1560) over a cache of 231 frames (360,360 keys), on sampled
+    rows."""
+    B, H, d, Lq = 1, 12, 128, 1560
+    Lk = 231 * Lq
+    g = torch.Generator(device=device())
+    g.manual_seed(231)
+    q = torch.randn((B, Lq, H, d), generator=g, device=device()).to(torch.bfloat16)
+    kc = torch.randn((B, Lk, H, d), generator=g, device=device()).to(torch.bfloat16)
+    vc = torch.randn((B, Lk, H, d), generator=g, device=device()).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lay.softmax_attention(q, kc, vc, out, 0)
+    torch.cuda.synchronize()
+    rows = sample_rows(Lq, 6, 5)
+    got = to_host(out)[0, rows]
+    qh = q.float().cpu().numpy()[0, rows]
+    for h in range(H):
+        ref = O.intra_attention(qh[:, h].astype(np.float64),
+                                kc[0, :, h].float().cpu().numpy().astype(np.float64),
+                                vc[0, :, h].float().cpu().numpy().astype(np.float64))
+        err = float(np.max(np.abs(got[:, h] - ref)) / np.max(np.abs(ref)))
+        assert err < TOL_OUT[SI.BF16], (h, err)

@@ -64,18 +64,11 @@ struct CombineKParams {
 // m_s. Lanes own queries and registers own d_v, as in the attention
 // kernel's accumulators, so the partials are read in the order they were
 // written and O_inter comes out of the MFMAs in the same layout.
-//
-// Item = (stream, head, query block, half): the workgroup forms output
-// columns d_v in [64*half, 64*half + 64) of its 128 queries. Q' needs every
-// feature, so both halves project q; each half reads its half of S and of
-// the partials. Wt: 32 KB of LDS for W_q[h], then the output rows; St:
-// 32 KB for bf16(S) (only the half's columns are filled).
+// Wt: 32 KB of LDS for W_q[h], then the output rows; St: 32 KB for bf16(S).
 __device__ __forceinline__ void combine_body(const CombineKParams p, int item, char *Wt,
                                              char *St) {
-  const int half = item & 1;
-  const int qitem = item >> 1;
-  const int qblk = qitem % p.nqblk;
-  const int bh = qitem / p.nqblk;
+  const int qblk = item % p.nqblk;
+  const int bh = item / p.nqblk;
   const int h = bh % p.H, b = bh / p.H;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
@@ -85,9 +78,8 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
 
   // Loads that do not depend on the inter-frame read go first: the merge
   // weights of the key ranges for this lane's query and the first range's
-  // partial (the half's four 16-byte units, in the order the attention
-  // kernel wrote them: unit 2*bb + r2 holds o[bb][8*r2 .. 8*r2+7]).
-  const int64_t blk0 = (int64_t)qitem * p.nsplit;
+  // partial (16-byte units in the order the attention kernel wrote them).
+  const int64_t blk0 = (int64_t)item * p.nsplit;
   const int qi = wave * 32 + l32;
   float mv[kMaxSplit], lv[kMaxSplit];
 #pragma unroll
@@ -97,16 +89,14 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
       mv[s] = ml[0];
       lv[s] = ml[1];
     }
-  const char *src =
-      p.ws_o + blk0 * kPartialOBytes + ((wave * 8 + 4 * half) * 64 + lane) * 16;
-  bf16x8 cur[4], nxt[4];
+  const char *src = p.ws_o + blk0 * kPartialOBytes + (wave * 8 * 64 + lane) * 16;
+  bf16x8 cur[8], nxt[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) cur[u] = *(const bf16x8 *)(src + u * 64 * 16);
+  for (int u = 0; u < 8; ++u) cur[u] = *(const bf16x8 *)(src + u * 64 * 16);
 
-  f32x16 acc[2];
+  f32x16 acc[4];
   if (inter) {
-    // W_q[h] (copied straight into LDS, swizzled) and bf16 of the half's
-    // columns of S[b][h] (units 8*half .. 8*half+7 of every row).
+    // W_q[h] (copied straight into LDS, swizzled) and bf16(S[b][h]).
     const bf16 *W = p.Wq + (int64_t)h * D * D;
     const int r4 = lane >> 4, pos = lane & 15;
 #pragma unroll
@@ -116,8 +106,8 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
     }
     const float *Sh = p.S + ((int64_t)b * p.H + h) * D * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 32 * i, u = 8 * half + (tid & 7);
+    for (int i = 0; i < 8; ++i) {
+      const int row = (tid >> 4) + 16 * i, u = tid & 15;
       const f32x4 x0 = *(const f32x4 *)(Sh + row * D + 8 * u);
       const f32x4 x1 = *(const f32x4 *)(Sh + row * D + 8 * u + 4);
       bf16x8 t;
@@ -163,26 +153,26 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
       for (int i = 0; i < 16; ++i) ss = fmaf(qp4[bb][i], qp4[bb][i], ss);
     ss += swap_halves(ss);
     const float inv = 1.f / fmaxf(sqrtf(ss), kL2Eps);
-    // O_inter^T = S^T Q'^T for the half's columns, Q' fed from the
-    // accumulators: register 8*(g%2) + j of block g/2 holds feature
-    // 16g + swap_bits23(8*(l/32) + j), i.e. rows 16g + 4*(l/32) + {0..3} and
-    // 16g + 8 + 4*(l/32) + {0..3} of S.
-    acc[0] = zero16();
-    acc[1] = zero16();
+    // O_inter^T = S^T Q'^T with Q' fed from the accumulators: register
+    // 8*(g%2) + j of block g/2 holds feature 16g + swap_bits23(8*(l/32) + j),
+    // i.e. rows 16g + 4*(l/32) + {0..3} and 16g + 8 + 4*(l/32) + {0..3} of S.
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) acc[bb] = zero16();
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       bf16x8 qb;
 #pragma unroll
       for (int j = 0; j < 8; ++j) qb[j] = (bf16)(qp4[g >> 1][8 * (g & 1) + j] * inv);
       const int k0 = 16 * g + 4 * hl;
-      const bf16x8 s0 = tile_col_operand(St, k0, k0 + 8, lane, 2 * half);
-      const bf16x8 s1 = tile_col_operand(St, k0, k0 + 8, lane, 2 * half + 1);
-      acc[0] = mfma32(s0, qb, acc[0]);
-      acc[1] = mfma32(s1, qb, acc[1]);
+      bf16x8 sa[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) sa[bb] = tile_col_operand(St, k0, k0 + 8, lane, bb);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) acc[bb] = mfma32(sa[bb], qb, acc[bb]);
     }
   } else {
-    acc[0] = zero16();
-    acc[1] = zero16();
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) acc[bb] = zero16();
   }
 
   float M = -INFINITY;
@@ -197,47 +187,47 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
       Lt += lv[s];
     }
   const float il = 1.f / Lt;
-  // acc += (w_s / sum w) Ohat_s, range by range, the next range's units in
-  // flight while the current one is added.
+  // acc += (w_s / sum w) Ohat_s, range by range, the next range's 16-byte
+  // units in flight while the current one is added.
 #pragma unroll
   for (int s = 0; s < kMaxSplit; ++s)
     if (s < p.nsplit) {
       if (s + 1 < p.nsplit) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
           nxt[u] = *(const bf16x8 *)(src + (s + 1) * kPartialOBytes + u * 64 * 16);
       }
       const float w = lv[s] * il;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            acc[j][8 * r2 + e] = fmaf(w, (float)cur[2 * j + r2][e], acc[j][8 * r2 + e]);
+            acc[bb][8 * r2 + e] = fmaf(w, (float)cur[2 * bb + r2][e], acc[bb][8 * r2 + e]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+      for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
     }
 
-  // Output through LDS: the wave's 32 rows (the half's 64 columns) in a
-  // swizzled tile in Wt (free once every wave is past the inter-frame
-  // read), then 16-byte units, 8 lanes per 128-byte row segment.
+  // Output rows through LDS: the wave's 32 rows as a swizzled 32 x 256-byte
+  // tile in Wt (free once every wave is past the inter-frame read), then
+  // 16-byte units, 16 lanes per 256-byte row.
   __syncthreads();
   char *ot = Wt + wave * 32 * 256;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       bf16x4 t;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = (bf16)acc[j][4 * r + e];
-      *(bf16x4 *)(ot + tile_off(l32, 4 * (2 * half + j) + r) + 8 * hl) = t;
+      for (int e = 0; e < 4; ++e) t[e] = (bf16)acc[bb][4 * r + e];
+      *(bf16x4 *)(ot + tile_off(l32, 4 * bb + r) + 8 * hl) = t;
     }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 8 * i + (lane >> 3), u = 8 * half + (lane & 7);
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * i + (lane >> 4), u = lane & 15;
     const int qr = qblk * kQBlock + wave * 32 + row;
     const bf16x8 t = *(const bf16x8 *)(ot + tile_off(row, u));
     if (qr < p.L) *(bf16x8 *)(p.out + ((int64_t)b * p.L + qr) * tok + (int64_t)h * D + 8 * u) = t;
@@ -532,7 +522,7 @@ hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_
   P.c.L = c.L;
   P.c.nqblk = c.plan.nqblk;
   P.c.nsplit = c.plan.nsplit;
-  P.c.nitems = 2 * c.B * c.H * c.plan.nqblk;
+  P.c.nitems = c.B * c.H * c.plan.nqblk;
   P.c.out = (bf16 *)c.out;
   P.per_xcd_c = (P.c.nitems + 7) / 8;
   P.d = DeltaKParams{};

@@ -71,7 +71,9 @@ def measured_traffic(kernel, workload, digest):
 
 
 def cpu_baseline(frames_host, W, w, budget_s=15.0, max_frames=400):
-    """Time the float64 oracle on host copies of the same frames."""
+    """Time the float64 oracle on host copies of the same frames. Workloads
+    whose full frame would not fit the budget are timed on one (stream,
+    head) of each pass and scaled by the number of (stream, head) pairs."""
     import numpy as np
     import oracle as O
     try:
@@ -79,18 +81,142 @@ def cpu_baseline(frames_host, W, w, budget_s=15.0, max_frames=400):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = os.cpu_count() or 1
-    S = np.zeros((w.B, w.H, w.d, w.d))
     Wf = W.astype(np.float64)
+    one_head = w.B * w.L > 1560
+    S = np.zeros((1, 1, w.d, w.d)) if one_head else np.zeros((w.B, w.H, w.d, w.d))
     done = 0
     t0 = time.perf_counter()
     while done < max_frames and (time.perf_counter() - t0) < budget_s:
         for p in frames_host[done % len(frames_host)]:
-            O.frame_forward(p["q"], p["k"], p["v"], Wf, S, p["alpha"], p["beta"], int(p["update"]))
+            if one_head:
+                sl = (slice(0, 1), slice(None), slice(0, 1))
+                O.frame_forward(p["q"][sl], p["k"][sl], p["v"][sl], Wf[:, 0:1], S,
+                                p["alpha"][0:1, 0:1], p["beta"][0:1, :, 0:1], int(p["update"]))
+            else:
+                O.frame_forward(p["q"], p["k"], p["v"], Wf, S, p["alpha"], p["beta"],
+                                int(p["update"]))
         done += 1
     dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} full frames ({w.noisy_passes} query-only + 1 clean pass each) of "
-                      f"{w.name}, all {w.H} heads, float64 NumPy/OpenBLAS, {dt:.1f} s"}
+    scale = w.B * w.H if one_head else 1
+    what = (f"one (stream, head) of {done} frames, scaled by {scale}" if one_head
+            else f"{done} full frames, all {w.B * w.H} (stream, head) pairs")
+    return {"value": done / dt / scale, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{what} ({w.noisy_passes} query-only + 1 clean pass each) of {w.name}, "
+                      f"float64 NumPy/OpenBLAS, {dt:.1f} s"}
+
+
+def per_frame_report(path):
+    """Long horizon: per-frame GPU latency and device memory of the layer and
+    of full-softmax attention over a growing key/value cache (the cached
+    clean keys/values of all previous frames plus the current pass's own)."""
+    import numpy as np
+    import torch
+
+    import synth_inputs as SI
+    from hybrid_softmax_gated_amd.layer import ARL2Layer, softmax_attention
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = SI.companion(SI.WORKLOADS["long231_480p"])
+    B, H, d, L = w.B, w.H, w.d, w.L
+    Wd = torch.from_numpy(SI.make_weights(w)).to(dev).to(torch.bfloat16)
+    out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def mem():
+        free, total = torch.cuda.mem_get_info()
+        return torch.cuda.memory_allocated(), total - free
+
+    # untimed warm-up of both paths (first launches, code loading)
+    warm = ARL2Layer(B, H, d, L, 0 if w.dtype == SI.BF16 else 1)
+    for q in SI.iter_passes_device(w, dev, frames=2):
+        warm.forward(q.q, q.k, q.v, Wd, q.alpha, q.beta, out, q.update)
+        softmax_attention(q.q, q.k, q.v, out, 0)
+    torch.cuda.synchronize()
+    del warm
+    torch.cuda.empty_cache()
+
+    res = {"workload": w.name, "frames": w.frames, "passes_per_frame": w.passes_per_frame,
+           "arl2_ms": [], "arl2_alloc": [], "arl2_used": [],
+           "kv_ms": [], "kv_alloc": [], "kv_used": [], "kv_cache_tokens": []}
+    # the layer
+    layer = ARL2Layer(B, H, d, L, 0 if w.dtype == SI.BF16 else 1)
+    cur = []
+    for p in SI.iter_passes_device(w, dev):
+        cur.append(p)
+        if not p.update:
+            continue
+        torch.cuda.synchronize()
+        ev[0].record()
+        for q in cur:
+            layer.forward(q.q, q.k, q.v, Wd, q.alpha, q.beta, out, q.update)
+        ev[1].record()
+        torch.cuda.synchronize()
+        res["arl2_ms"].append(ev[0].elapsed_time(ev[1]))
+        a, u = mem()
+        res["arl2_alloc"].append(a)
+        res["arl2_used"].append(u)
+        cur = []
+    del layer
+    torch.cuda.empty_cache()
+    # The comparator: every pass attends over the cached clean keys/values of
+    # all previous frames followed by its own. The cache grows by one frame
+    # per frame, in a buffer whose capacity doubles when full (so device
+    # memory grows with the frame index while copies stay amortised).
+    cap = 1
+    kc = torch.empty((B, cap * L, H, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    cur = []
+    nf = 0
+    for p in SI.iter_passes_device(w, dev):
+        cur.append(p)
+        if not p.update:
+            continue
+        if nf + 1 > cap:
+            cap *= 2
+            k2 = torch.empty((B, cap * L, H, d), dtype=torch.bfloat16, device=dev)
+            v2 = torch.empty_like(k2)
+            k2[:, :nf * L] = kc[:, :nf * L]
+            v2[:, :nf * L] = vc[:, :nf * L]
+            kc, vc = k2, v2
+            del k2, v2
+        lk = (nf + 1) * L
+        torch.cuda.synchronize()
+        ms = 0.0
+        for q in cur:
+            kc[:, nf * L:lk] = q.k
+            vc[:, nf * L:lk] = q.v
+            ev[2].record()
+            softmax_attention(q.q, kc[:, :lk], vc[:, :lk], out, 0)
+            ev[3].record()
+            torch.cuda.synchronize()
+            ms += ev[2].elapsed_time(ev[3])
+        nf += 1  # the clean pass's keys/values stay in the cache
+        res["kv_ms"].append(ms)
+        a, u = mem()
+        res["kv_alloc"].append(a)
+        res["kv_used"].append(u)
+        res["kv_cache_tokens"].append(nf * L)
+        cur = []
+    with open(path, "w") as f:
+        json.dump(res, f)
+    n = len(res["arl2_ms"])
+    pick = [0, 9, 49, 99, n - 1]
+    summ = {"metric": "per-frame GPU latency and device memory vs frame index, long horizon "
+                      "(231 frames x (1 query-only + 1 clean pass), 12 heads, d=128, L=1560)",
+            "frames": n,
+            "arl2_ms": {i + 1: round(res["arl2_ms"][i], 4) for i in pick},
+            "kv_cache_ms": {i + 1: round(res["kv_ms"][i], 4) for i in pick},
+            "arl2_allocated_mb": {i + 1: round(res["arl2_alloc"][i] / 1e6, 3) for i in pick},
+            "kv_cache_allocated_mb": {i + 1: round(res["kv_alloc"][i] / 1e6, 3) for i in pick},
+            "kv_cache_live_mb": {i + 1: round(res["kv_cache_tokens"][i] * H * d * 4 / 1e6, 3)
+                                 for i in pick},
+            "speedup_at_last_frame": round(res["kv_ms"][-1] / res["arl2_ms"][-1], 2),
+            "cumulative_ms": {"arl2": round(sum(res["arl2_ms"]), 2),
+                              "kv_cache": round(sum(res["kv_ms"]), 2)},
+            "detail": path}
+    print(json.dumps(summ), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -100,6 +226,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="frame_step_480p",
                     choices=["frame_step_480p", "stream21_480p", "batched720p"])
+    ap.add_argument("--per-frame-report", metavar="PATH", default="",
+                    help="instead of the throughput line: run the 231-frame long-horizon "
+                         "schedule through the layer and through full-softmax attention over a "
+                         "key/value cache that grows by one frame per frame, and write per-frame "
+                         "GPU latency and device memory of both to PATH (JSON)")
     ap.add_argument("--profile-steps", type=int, default=100)
     ap.add_argument("--profile-repeat", type=int, default=10,
                     help="back-to-back launches of each idempotent kernel per event pair "
@@ -124,6 +255,8 @@ def main() -> int:
               "(heads and streams shard with no exchange; see the sharding note in the design)",
               file=sys.stderr)
         return 2
+    if args.per_frame_report:
+        return per_frame_report(args.per_frame_report)
 
     import numpy as np
     import torch

@@ -92,6 +92,8 @@ def _ptr(x):
         return None
     if isinstance(x, int):
         return x
+    if hasattr(x, "is_contiguous") and not x.is_contiguous():
+        raise ValueError("libarl2 takes contiguous tensors (call .contiguous() first)")
     return int(x.data_ptr())
 
 

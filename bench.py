@@ -226,6 +226,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="frame_step_480p",
                     choices=["frame_step_480p", "stream21_480p", "batched720p"])
+    ap.add_argument("--gate", default="headwise", choices=["headwise", "elementwise"],
+                    help="forget gate: one scalar per head (the method's) or one value per "
+                         "d_k row (the ablation's)")
     ap.add_argument("--per-frame-report", metavar="PATH", default="",
                     help="instead of the throughput line: run the 231-frame long-horizon "
                          "schedule through the layer and through full-softmax attention over a "
@@ -268,7 +271,9 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = SI.companion(SI.WORKLOADS[args.workload])
+    w = SI.scaled(SI.companion(SI.WORKLOADS[args.workload]), gate=args.gate)
+    if args.gate != "headwise":
+        w = SI.scaled(w, name=f"{w.name}_{args.gate}_gate")
     B, H, d, L = w.B, w.H, w.d, w.L
 
     # ---- inputs, resident in HBM before timing
@@ -288,7 +293,7 @@ def main() -> int:
 
     def step(i):
         for p in frames[i % len(frames)]:
-            layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, stream)
+            layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, stream, gate=w.gate)
 
     for i in range(args.warmup):
         step(i)

@@ -23,6 +23,8 @@ ARL2_ERR_UNSUPPORTED = 2
 ARL2_ERR_HIP = 3
 ARL2_BF16 = 0
 ARL2_F32 = 1
+ARL2_GATE_HEADWISE = 0
+ARL2_GATE_ELEMENTWISE = 1
 
 # The in-tree library; ARL2_LIBRARY may name another build of the same ABI
 # (for comparing kernel variants).
@@ -66,6 +68,8 @@ def _load() -> ctypes.CDLL:
         "arl2_state_init": (I, [ctypes.POINTER(arl2_state), I, I, I, I, I, P, P, Z, P]),
         "arl2_state_reset": (I, [ctypes.POINTER(arl2_state), P, P]),
         "arl2_frame_forward": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, P, P, I, P]),
+        "arl2_frame_forward_gated": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, I, P, P, I,
+                                         P]),
         "arl2_softmax_attention_workspace_bytes": (Z, [I, I, I, I, I, I]),
         "arl2_softmax_attention": (I, [P, P, P, I, I, I, I, I, I, P, P, Z, P]),
         "arl2_profile_enable": (I, [I, I]),
@@ -82,7 +86,7 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 
 EXPORTED = ("arl2_version", "arl2_status_string", "arl2_last_error", "arl2_workspace_bytes",
-            "arl2_state_init", "arl2_state_reset", "arl2_frame_forward",
+            "arl2_state_init", "arl2_state_reset", "arl2_frame_forward", "arl2_frame_forward_gated",
             "arl2_softmax_attention_workspace_bytes", "arl2_softmax_attention",
             "arl2_profile_enable", "arl2_profile_report", "arl2_profile_reset")
 
@@ -145,6 +149,13 @@ def arl2_frame_forward(q, k, v, Wphi, st: arl2_state, alpha, beta, out, update_f
     _check(_lib.arl2_frame_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(Wphi), ctypes.byref(st),
                                    _ptr(alpha), _ptr(beta), _ptr(out), update_flag,
                                    _stream(stream)))
+
+
+def arl2_frame_forward_gated(q, k, v, Wphi, st: arl2_state, alpha, gate: int, beta, out,
+                             update_flag: int, stream=None) -> None:
+    _check(_lib.arl2_frame_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(Wphi), ctypes.byref(st),
+                                         _ptr(alpha), gate, _ptr(beta), _ptr(out), update_flag,
+                                         _stream(stream)))
 
 
 def arl2_softmax_attention_workspace_bytes(B: int, H: int, d: int, Lq: int, Lk: int,

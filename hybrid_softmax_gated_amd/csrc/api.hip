@@ -306,14 +306,18 @@ arl2_status arl2_state_reset(arl2_state *st, const float *S0_dev, void *stream) 
   return ok();
 }
 
-arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, const void *Wphi,
-                               arl2_state *st, const float *alpha, const float *beta, void *out,
-                               int32_t update_flag, void *stream) {
-  const char *fn = "arl2_frame_forward";
+namespace {
+
+arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, const void *v,
+                               const void *Wphi, arl2_state *st, const float *alpha,
+                               int32_t gate, const float *beta, void *out, int32_t update_flag,
+                               void *stream) {
   arl2_status cs = check_state(st, fn);
   if (cs != ARL2_OK) return cs;
   if (update_flag != 0 && update_flag != 1)
     return fail(ARL2_ERR_INVALID_ARG, "%s: update_flag %d is not 0 or 1", fn, update_flag);
+  if (gate != ARL2_GATE_HEADWISE && gate != ARL2_GATE_ELEMENTWISE)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: gate %d is not a gate kind", fn, gate);
   const void *tens[5] = {q, k, v, Wphi, out};
   const char *names[5] = {"q", "k", "v", "Wphi", "out"};
   for (int i = 0; i < 5; ++i) {
@@ -344,7 +348,8 @@ arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, cons
                   fn);
     if (!aligned(alpha, 4) || !aligned(beta, 4))
       return fail(ARL2_ERR_INVALID_ARG, "%s: alpha/beta are misaligned", fn);
-    const Range r_a = range(alpha, (size_t)B * H * 4), r_b = range(beta, (size_t)B * L * H * 4);
+    const size_t abytes = (size_t)B * H * (gate == ARL2_GATE_ELEMENTWISE ? d : 1) * 4;
+    const Range r_a = range(alpha, abytes), r_b = range(beta, (size_t)B * L * H * 4);
     if (overlap(r_a, r_S) || overlap(r_b, r_S) || overlap(r_a, r_ws) || overlap(r_b, r_ws))
       return fail(ARL2_ERR_INVALID_ARG, "%s: alpha/beta overlap the state or its workspace", fn);
   }
@@ -393,11 +398,29 @@ arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, cons
   }
   if (update_flag) {
     if ((e = timed("delta_apply", s, [&] {
-           return arl2::launch_delta_apply(S, alpha, ws_ds, iB, iH, id, fp.nchunk, s);
+           return arl2::launch_delta_apply(S, alpha, gate == ARL2_GATE_ELEMENTWISE, ws_ds, iB, iH,
+                                           id, fp.nchunk, s);
          }, /*idempotent=*/false)))
       return hip_status(e, fn);
   }
   return ok();
+}
+
+}  // namespace
+
+arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, const void *Wphi,
+                               arl2_state *st, const float *alpha, const float *beta, void *out,
+                               int32_t update_flag, void *stream) {
+  return frame_forward_impl("arl2_frame_forward", q, k, v, Wphi, st, alpha, ARL2_GATE_HEADWISE,
+                            beta, out, update_flag, stream);
+}
+
+arl2_status arl2_frame_forward_gated(const void *q, const void *k, const void *v,
+                                     const void *Wphi, arl2_state *st, const float *alpha,
+                                     int32_t gate, const float *beta, void *out,
+                                     int32_t update_flag, void *stream) {
+  return frame_forward_impl("arl2_frame_forward_gated", q, k, v, Wphi, st, alpha, gate, beta,
+                            out, update_flag, stream);
 }
 
 size_t arl2_softmax_attention_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t Lq,

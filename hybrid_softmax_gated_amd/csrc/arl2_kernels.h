@@ -73,10 +73,11 @@ struct DeltaArgs {
 hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_t s);
 
 // ---------------------------------------------------------------- shared
-// S[b][h] := alpha[b][h] * S[b][h] + sum over chunks c (in order) of
-// ws_dS[b][h][c], elementwise.
-hipError_t launch_delta_apply(float *S, const float *alpha, const float *ws_dS, int B, int H,
-                              int d, int nchunk, hipStream_t s);
+// S[b][h] := gate(S[b][h]) + sum over chunks c (in order) of ws_dS[b][h][c],
+// with gate(S) = alpha[b][h] * S (headwise) or row i scaled by
+// alpha[b][h][i] (elementwise).
+hipError_t launch_delta_apply(float *S, const float *alpha, bool elementwise, const float *ws_dS,
+                              int B, int H, int d, int nchunk, hipStream_t s);
 // dst[i] := src ? src[i] : 0 for i < n.
 hipError_t launch_fill_state(float *dst, const float *src, int64_t n, hipStream_t s);
 

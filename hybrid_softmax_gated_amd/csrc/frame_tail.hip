@@ -479,7 +479,8 @@ __global__ __launch_bounds__(256, 2) void tail_kernel(TailKParams P) {
 // the chunk partials are summed in chunk order, with up to 16 loads in
 // flight per thread.
 __global__ __launch_bounds__(64) void delta_apply_kernel(float *S, const float *alpha,
-                                                         const float *ws, int dd4, int nchunk) {
+                                                         int arow4, const float *ws, int dd4,
+                                                         int nchunk) {
   const int e = blockIdx.x * 64 + threadIdx.x;
   const int bh = blockIdx.y;
   if (e >= dd4) return;
@@ -496,7 +497,9 @@ __global__ __launch_bounds__(64) void delta_apply_kernel(float *S, const float *
     for (int u = 0; u < 16; ++u)
       if (c0 + u < nchunk) acc += t[u];
   }
-  const float a = alpha[bh];
+  // Headwise: one gate per (stream, head) (arow4 = 0). Elementwise: one gate
+  // per d_k row; a row holds arow4 groups of 4 values.
+  const float a = arow4 ? alpha[(int64_t)bh * (dd4 / arow4) + e / arow4] : alpha[bh];
   f32x4 r;
 #pragma unroll
   for (int u = 0; u < 4; ++u) r[u] = fmaf(a, sv[u], acc[u]);
@@ -548,11 +551,12 @@ hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_delta_apply(float *S, const float *alpha, const float *ws_dS, int B, int H,
-                              int d, int nchunk, hipStream_t s) {
+hipError_t launch_delta_apply(float *S, const float *alpha, bool elementwise, const float *ws_dS,
+                              int B, int H, int d, int nchunk, hipStream_t s) {
   const int dd4 = d * d / 4;
   dim3 grid((unsigned)((dd4 + 63) / 64), (unsigned)(B * H));
-  hipLaunchKernelGGL(delta_apply_kernel, grid, dim3(64), 0, s, S, alpha, ws_dS, dd4, nchunk);
+  hipLaunchKernelGGL(delta_apply_kernel, grid, dim3(64), 0, s, S, alpha, elementwise ? d / 4 : 0,
+                     ws_dS, dd4, nchunk);
   return hipGetLastError();
 }
 

@@ -27,8 +27,15 @@ class ARL2Layer:
     def reset(self, S0=None, stream=None) -> None:
         B.arl2_state_reset(self.st, S0, stream)
 
-    def forward(self, q, k, v, W, alpha, beta, out, update: bool, stream=None) -> None:
-        B.arl2_frame_forward(q, k, v, W, self.st, alpha, beta, out, 1 if update else 0, stream)
+    def forward(self, q, k, v, W, alpha, beta, out, update: bool, stream=None,
+                gate: str = "headwise") -> None:
+        """One pass; gate "elementwise" takes alpha [B][H][d] (one gate per
+        d_k row) instead of [B][H]."""
+        if gate == "headwise":
+            B.arl2_frame_forward(q, k, v, W, self.st, alpha, beta, out, 1 if update else 0, stream)
+        else:
+            B.arl2_frame_forward_gated(q, k, v, W, self.st, alpha, B.ARL2_GATE_ELEMENTWISE, beta,
+                                       out, 1 if update else 0, stream)
 
 
 def softmax_attention(q, kc, vc, out, dtype: int, ws=None, stream=None):

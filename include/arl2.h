@@ -142,6 +142,32 @@ ARL2_API arl2_status arl2_frame_forward(const void *q, const void *k, const void
                                arl2_state *st, const float *alpha, const float *beta,
                                void *out, int32_t update_flag, void *stream);
 
+/* Forget-gate kinds of arl2_frame_forward_gated. */
+typedef enum {
+  ARL2_GATE_HEADWISE = 0,   /* alpha [B][H]: one scalar per stream, head and frame       */
+  ARL2_GATE_ELEMENTWISE = 1 /* alpha [B][H][d]: one value per d_k row of the state      */
+} arl2_gate;
+
+/*
+ * arl2_frame_forward with a choice of forget gate. The pages' ablation
+ * ("Technical Summary ...", section 4 "Experimental Results", Ablations;
+ * atlas.scime.ai summary, "Surprising findings") compares the method's
+ * headwise gate with elementwise gating and prints no formula for the
+ * latter; this library reads it as one gate per key channel:
+ *   S_N = diag(alpha) S_{N-1} + K'^T diag(beta) (V' - K' S_{N-1}),
+ * i.e. row i (d_k index) of the carried state is scaled by alpha[b][h][i];
+ * the residual reads the ungated S_{N-1}.
+ *   gate   ARL2_GATE_HEADWISE: alpha is device [B][H] float32 and the call is
+ *          exactly arl2_frame_forward. ARL2_GATE_ELEMENTWISE: alpha is device
+ *          [B][H][d] float32.
+ * Every other argument, the layout, ownership and the errors are those of
+ * arl2_frame_forward; a gate outside arl2_gate is INVALID_ARG.
+ */
+ARL2_API arl2_status arl2_frame_forward_gated(const void *q, const void *k, const void *v,
+                                     const void *Wphi, arl2_state *st, const float *alpha,
+                                     int32_t gate, const float *beta, void *out,
+                                     int32_t update_flag, void *stream);
+
 /*
  * Full-softmax attention of Lq queries over Lk cached keys/values per stream
  * and head, with scale 1/sqrt(d) and no mask: the growing key/value-cache

@@ -8,6 +8,7 @@ from .arl2_oracle import (  # noqa: F401
     delta_update,
     feature_map,
     frame_forward,
+    gate_state,
     head_forward,
     inter_read,
     intra_attention,

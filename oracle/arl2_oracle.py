@@ -90,20 +90,39 @@ def inter_read(Qp: np.ndarray, S: np.ndarray) -> np.ndarray:
     return Qp @ S
 
 
-def delta_update(S: np.ndarray, Kp: np.ndarray, Vp: np.ndarray, alpha: float,
+def gate_state(S: np.ndarray, alpha) -> np.ndarray:
+    """The forget gate's action on the state.
+
+    Headwise gating (the method's choice, [TS] section 4 and [AS]
+    "Surprising findings"): alpha is one scalar per head and frame and
+    scales the whole state. Elementwise gating (the ablation those passages
+    compare against): the pages give no formula; the reading here is one
+    gate per key channel, alpha [d_k], scaling row i of S (d_k x d_v) by
+    alpha_i, i.e. diag(alpha) S.
+    """
+    a = np.asarray(alpha, dtype=np.float64)
+    if a.ndim == 0:
+        return float(a) * S
+    assert a.shape == (S.shape[0],), "elementwise gate: one value per d_k row"
+    return a[:, None] * S
+
+
+def delta_update(S: np.ndarray, Kp: np.ndarray, Vp: np.ndarray, alpha,
                  beta: np.ndarray) -> np.ndarray:
     """Gated delta state update of [TS] section 2.1, one frame:
 
         R   = V' - K' S_{N-1}                     (residual of every token)
-        S_N = alpha S_{N-1} + K'^T diag(beta) R
+        S_N = gate(S_{N-1}) + K'^T diag(beta) R,  gate(S) = alpha S
 
     S [d_k][d_v], Kp [L][d_k], Vp [L][d_v], alpha a scalar (headwise gate of
-    this frame), beta [L] (one learning rate per token). The printed formula
-    omits the transpose; with tokens as rows of K' the product that yields a
-    d_k x d_v matrix is K'^T (...). Returns the new state (a new array).
+    this frame; or [d_k] for elementwise gating, see gate_state), beta [L]
+    (one learning rate per token). The printed formula omits the transpose;
+    with tokens as rows of K' the product that yields a d_k x d_v matrix is
+    K'^T (...). The gate acts on the carried state only; the residual reads
+    the ungated S_{N-1}. Returns the new state (a new array).
     """
     R = Vp - Kp @ S
-    return alpha * S + Kp.T @ (beta[:, None] * R)
+    return gate_state(S, alpha) + Kp.T @ (beta[:, None] * R)
 
 
 def token_level_update(S: np.ndarray, Kp: np.ndarray, Vp: np.ndarray, alpha: float,
@@ -127,7 +146,7 @@ def token_level_update(S: np.ndarray, Kp: np.ndarray, Vp: np.ndarray, alpha: flo
 
 # ------------------------------------------------------------ one layer
 def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, Wq: np.ndarray,
-                 Wk: np.ndarray, Wv: np.ndarray, S: np.ndarray, alpha: float,
+                 Wk: np.ndarray, Wv: np.ndarray, S: np.ndarray, alpha,
                  beta: np.ndarray, update: bool) -> Tuple[np.ndarray, np.ndarray]:
     """One pass of one head of one stream.
 
@@ -154,7 +173,8 @@ def frame_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, Wphi: np.ndarray,
     q, k, v [B][L][H][d] (token-major); Wphi [3][H][d][d] (maps for q, k, v);
     S [B][H][d][d] float64, updated IN PLACE when ``update_flag`` is 1 and
     left untouched when it is 0 ([TS] section 2.2: denoising passes only
-    read, the clean pass writes); alpha [B][H]; beta [B][L][H].
+    read, the clean pass writes); alpha [B][H] (headwise) or [B][H][d]
+    (elementwise, see gate_state); beta [B][L][H].
     Returns out [B][L][H][d] float64.
     """
     assert update_flag in (0, 1)
@@ -167,7 +187,7 @@ def frame_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, Wphi: np.ndarray,
     new_states = {}
     for b in range(B):
         for h in range(H):
-            a = float(alpha[b][h]) if update_flag else 0.0
+            a = np.asarray(alpha[b][h], dtype=np.float64) if update_flag else 0.0
             be = np.asarray(beta[b][:, h], dtype=np.float64) if update_flag else None
             o, s_next = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], W[0, h], W[1, h],
                                      W[2, h], S[b, h], a, be, bool(update_flag))

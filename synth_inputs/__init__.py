@@ -12,8 +12,9 @@ Workload recipe (the pages give the model shape, not the activations):
 * phi weights W = I + N(0, 0.01) (the second argument is a standard
   deviation), one d x d map per (map in {q, k, v}, head), layout [3][H][d][d],
   drawn once per run and shared by every stream of a batch.
-* alpha = sigmoid(N(2, 0.5)) per (stream, head, frame), beta = sigmoid(N(0, 1))
-  per (stream, token, head, frame), fp32.
+* alpha = sigmoid(N(2, 0.5)) per (stream, head, frame) (per (stream, head,
+  frame, d_k row) for elementwise gating), beta = sigmoid(N(0, 1)) per
+  (stream, token, head, frame), fp32.
 * S0 = 0, or N(0, 0.02) per element where a workload asks for a warm state.
 * For bf16 workloads every io tensor (q, k, v, W) is drawn in float32 and
   rounded to bfloat16 with round-to-nearest-even; the float32 arrays returned
@@ -92,6 +93,7 @@ class Workload:
     seed: int = 0          # stream b uses seed + b
     beta_scale: float = 1.0  # companion runs multiply beta by 1/L
     w_std: float = 0.01
+    gate: str = "headwise"   # "elementwise": alpha has one value per d_k row
 
     @property
     def passes_per_frame(self) -> int:
@@ -132,7 +134,7 @@ class PassInputs:
     q: np.ndarray
     k: np.ndarray
     v: np.ndarray
-    alpha: np.ndarray      # [B][H] float32 (this frame's)
+    alpha: np.ndarray      # [B][H] (headwise) or [B][H][d] (elementwise) float32
     beta: np.ndarray       # [B][L][H] float32 (this frame's)
     dtype: str
 
@@ -182,7 +184,9 @@ def iter_passes(w: Workload, frames: Optional[int] = None) -> Iterator[PassInput
                 x = np.stack([r.standard_normal(shape, dtype=np.float32) for r in rngs])
                 qkv.append(_store(x, w.dtype))
             per_pass.append(qkv)
-        alpha = np.stack([_sigmoid(2.0 + 0.5 * r.standard_normal(w.H, dtype=np.float32)) for r in rngs])
+        ashape = (w.H, w.d) if w.gate == "elementwise" else (w.H,)
+        alpha = np.stack([_sigmoid(2.0 + 0.5 * r.standard_normal(ashape, dtype=np.float32))
+                          for r in rngs])
         beta = np.stack([_sigmoid(r.standard_normal((w.L, w.H), dtype=np.float32)) for r in rngs])
         if w.beta_scale != 1.0:
             beta = (beta * np.float32(w.beta_scale)).astype(np.float32)
@@ -241,10 +245,11 @@ def iter_passes_device(w: Workload, device, frames: Optional[int] = None) -> Ite
     io = torch_dtype(w.dtype)
     shape = (w.L, w.H, w.d)
     for f in range(nf):
-        alpha = torch.empty((w.B, w.H), dtype=torch.float32, device=device)
+        ashape = (w.H, w.d) if w.gate == "elementwise" else (w.H,)
+        alpha = torch.empty((w.B,) + ashape, dtype=torch.float32, device=device)
         beta = torch.empty((w.B, w.L, w.H), dtype=torch.float32, device=device)
         for b, g in enumerate(gens):
-            alpha[b] = torch.sigmoid(2.0 + 0.5 * torch.randn(w.H, generator=g, device=device))
+            alpha[b] = torch.sigmoid(2.0 + 0.5 * torch.randn(ashape, generator=g, device=device))
             beta[b] = torch.sigmoid(torch.randn((w.L, w.H), generator=g, device=device))
         if w.beta_scale != 1.0:
             beta *= w.beta_scale

@@ -63,7 +63,7 @@ def oracle_state_update(S: np.ndarray, k: np.ndarray, v: np.ndarray, W: np.ndarr
         for h in range(H):
             Kp = O.l2_normalize_rows(O.feature_map(k[b, :, h], W[1, h]))
             Vp = O.feature_map(v[b, :, h], W[2, h])
-            S[b, h] = O.delta_update(S[b, h], Kp, Vp, float(alpha[b, h]), beta[b, :, h])
+            S[b, h] = O.delta_update(S[b, h], Kp, Vp, alpha[b, h], beta[b, :, h])
 
 
 def oracle_rows(q, k, v, W, S, rows_per_head: np.ndarray):

@@ -31,8 +31,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     assert {"arl2_state_init", "arl2_state_reset", "arl2_frame_forward",
-            "arl2_workspace_bytes"} <= names
-    assert len(names) == 12
+            "arl2_frame_forward_gated", "arl2_workspace_bytes"} <= names
+    assert len(names) == 13
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -148,6 +148,18 @@ def test_frame_forward_validation(B):
     st2 = _fake_state(B, d=32)
     assert _code(B.arl2_frame_forward, Q, K, V, W, st2, AL, BE, OUT, 0)[0] == B.ARL2_ERR_UNSUPPORTED
     assert B.arl2_last_error()  # the detail of the last failure is kept
+
+
+def test_gated_frame_forward_validation(B):
+    st = _fake_state(B)
+    E = B.ARL2_ERR_INVALID_ARG
+    g = B.arl2_frame_forward_gated
+    assert "gate" in _code(g, Q, K, V, W, st, AL, 2, BE, OUT, 1)[1]
+    assert _code(g, Q, K, V, W, st, AL, -1, BE, OUT, 0)[0] == E
+    assert _code(g, Q, K, V, W, st, None, B.ARL2_GATE_ELEMENTWISE, BE, OUT, 1)[0] == E
+    # an elementwise alpha ([B][H][d] floats) that reaches into the state
+    assert _code(g, Q, K, V, W, st, FAKE_S - 512, B.ARL2_GATE_ELEMENTWISE, BE, OUT, 1)[0] == E
+    assert _code(g, Q, K, V, W, st, AL, B.ARL2_GATE_HEADWISE, BE, OUT, 7)[0] == E
 
 
 def test_state_reset_validation(B):

@@ -197,6 +197,68 @@ def test_single_token_general_gates():
             assert abs(S1[i, j] - (a * S0[i, j] + b * k[i] * (v[j] - pred))) < 1e-14
 
 
+# ------------------------------------------------ elementwise gating (ablation)
+def test_elementwise_gate_single_token_by_loops():
+    """L = 1 with one gate per d_k row: S1[i][j] = a_i S0[i][j] +
+    beta k_i (v_j - sum_t k_t S0[t][j]), element by element with loops (the
+    gate scales the carried state's rows; the residual reads S0 ungated)."""
+    r = _rng(31)
+    d = 5
+    S0 = r.normal(size=(d, d))
+    k = _unit_rows(r.normal(size=(1, d)))[0]
+    v = r.normal(size=d)
+    a = np.array([0.9, 0.5, 0.1, 1.0, 0.3])
+    b = 0.4
+    S1 = O.delta_update(S0, k[None], v[None], a, np.array([b]))
+    for i in range(d):
+        for j in range(d):
+            pred = sum(k[t] * S0[t, j] for t in range(d))
+            assert abs(S1[i, j] - (a[i] * S0[i, j] + b * k[i] * (v[j] - pred))) < 1e-14
+
+
+def test_elementwise_gate_with_equal_entries_is_headwise():
+    r = _rng(32)
+    L, d = 40, 8
+    S = r.normal(size=(d, d))
+    Kp = _unit_rows(r.normal(size=(L, d)))
+    Vp = r.normal(size=(L, d))
+    beta = r.uniform(0, 1, size=L)
+    for c in (0.0, 0.37, 1.0):
+        got = O.delta_update(S, Kp, Vp, np.full(d, c), beta)
+        assert np.array_equal(got, O.delta_update(S, Kp, Vp, c, beta))
+
+
+def test_elementwise_gate_one_and_zero_beta_leaves_state_bitwise():
+    r = _rng(33)
+    S = r.normal(size=(6, 6))
+    Kp = _unit_rows(r.normal(size=(9, 6)))
+    got = O.delta_update(S, Kp, r.normal(size=(9, 6)), np.ones(6), np.zeros(9))
+    assert np.array_equal(got, S)
+
+
+def test_frame_forward_takes_elementwise_gates_per_stream_and_head():
+    """alpha [B][H][d] in the layer call gives, per (stream, head), the
+    single-head update with that head's vector."""
+    w = SI_scaled_elementwise()
+    W = make_weights(w).astype(np.float64)
+    p = next(p for p in iter_passes(w) if p.update)
+    S = np.random.default_rng(5).normal(size=(w.B, w.H, w.d, w.d))
+    S_ref = S.copy()
+    O.frame_forward(p.q, p.k, p.v, W, S, p.alpha, p.beta, 1)
+    assert p.alpha.shape == (w.B, w.H, w.d)
+    for b in range(w.B):
+        for h in range(w.H):
+            Kp = O.l2_normalize_rows(O.feature_map(p.k[b, :, h].astype(np.float64), W[1, h]))
+            Vp = O.feature_map(p.v[b, :, h].astype(np.float64), W[2, h])
+            ref = O.delta_update(S_ref[b, h], Kp, Vp, p.alpha[b, h], p.beta[b, :, h])
+            assert np.array_equal(S[b, h], ref)
+
+
+def SI_scaled_elementwise():
+    import synth_inputs as SI
+    return SI.Workload("gate", 2, 3, 16, 20, 1, 0, SI.F32, 0.0, seed=4, gate="elementwise")
+
+
 # ------------------------------------------------------------ P6: gradient
 def test_update_is_one_gradient_step_autograd():
     torch = pytest.importorskip("torch")
@@ -385,6 +447,10 @@ def _planted_variants():
     def l2_missing(x, eps=1e-6):
         return x
 
+    def gate_on_columns(S, alpha):            # elementwise gate scales d_v, not d_k
+        a = np.asarray(alpha, dtype=np.float64)
+        return float(a) * S if a.ndim == 0 else S * a[None, :]
+
     return {
         "softmax scale dropped": ("intra_attention", sm_noscale),
         "K' not transposed": ("delta_update", upd_no_transpose),
@@ -394,6 +460,7 @@ def _planted_variants():
         "beta misindexed": ("delta_update", upd_beta_reversed),
         "feature map transposed": ("feature_map", fmap_transposed),
         "L2 normalisation dropped": ("l2_normalize_rows", l2_missing),
+        "elementwise gate on the wrong axis": ("gate_state", gate_on_columns),
     }
 
 
@@ -401,7 +468,7 @@ def _pin_suite():
     """The pins above that are sensitive to the planted slips."""
     return [test_worked_example_d2_state_and_read, test_update_is_one_gradient_step_autograd,
             test_consistent_memory_only_decays, test_single_token_general_gates,
-            test_token_permutation_equivariance]
+            test_token_permutation_equivariance, test_elementwise_gate_single_token_by_loops]
 
 
 @pytest.mark.parametrize("label", list(_planted_variants().keys()))

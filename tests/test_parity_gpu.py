@@ -47,7 +47,7 @@ def _run_stream(lay, torch, w, frames=None, S0=None, check_every_pass=True):
         q, k, v = (to_dev(x, w.dtype) for x in (p.q, p.k, p.v))
         al = torch.from_numpy(p.alpha).to(device())
         be = torch.from_numpy(p.beta).to(device())
-        L.forward(q, k, v, Wd, al, be, out, p.update)
+        L.forward(q, k, v, Wd, al, be, out, p.update, gate=w.gate)
         ref = O.frame_forward(p.q, p.k, p.v, W, S_ref, p.alpha, p.beta, int(p.update))
         torch.cuda.synchronize()
         if check_every_pass or p.update:
@@ -110,6 +110,33 @@ def test_generic_paths(lay, torch, dtype, d, L):
     print(f"{dtype} d={d} L={L} out {max(eo):.2e} S {max(es):.2e}")
     assert max(eo) < TOL_OUT[dtype]
     assert max(es) < TOL_S
+
+
+@pytest.mark.parametrize("dtype,d,B,H,L", [(SI.BF16, 128, 2, 3, 200), (SI.F32, 16, 2, 2, 50),
+                                           (SI.BF16, 128, 1, 12, 1560)])
+def test_elementwise_gate(lay, torch, dtype, d, B, H, L):
+    """The ablation's elementwise forget gate (one value per d_k row), on the
+    MFMA path (bf16, d = 128) and the generic path (f32, d = 16)."""
+    w = SI.Workload("gate", B, H, d, L, 3, 1, dtype, 0.02, seed=d + L, gate="elementwise")
+    eo, es, _, _ = _run_stream(lay, torch, w)
+    print(f"elementwise gate {dtype} d={d} L={L}: out {max(eo):.2e} S {max(es):.2e}")
+    assert max(eo) < TOL_OUT[dtype]
+    assert max(es) < TOL_S
+
+
+def test_elementwise_gate_with_equal_entries_matches_headwise_bitwise(lay, torch):
+    B, H, d, L = 2, 3, 128, 300
+    p, W, (q, k, v, Wd), al, be = _one_pass_inputs(torch, B, H, d, L, SI.BF16, 21)
+    res = []
+    for gate in ("headwise", "elementwise"):
+        layer = lay.ARL2Layer(B, H, d, L, 0)
+        layer.reset(torch.full((B, H, d, d), 0.01, device=device()))
+        a = al if gate == "headwise" else al[:, :, None].expand(B, H, d).contiguous()
+        out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=device())
+        layer.forward(q, k, v, Wd, a, be, out, True, gate=gate)
+        torch.cuda.synchronize()
+        res.append(layer.S.clone())
+    assert torch.equal(res[0].view(torch.int32), res[1].view(torch.int32))
 
 
 def _one_pass_inputs(torch, B, H, d, L, dtype, seed):

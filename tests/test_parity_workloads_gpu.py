@@ -75,7 +75,7 @@ def _stream(lay, torch, w, frames=None, rows_n=12, out_every=1, until_overflow=F
     for p in SI.iter_passes_device(w, device(), frames):
         ref_finite = bool(np.max(np.abs(S_ref)) < FP32_MAX)
         ev[0].record()
-        layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update)
+        layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, gate=w.gate)
         ev[1].record()
         torch.cuda.synchronize()
         t_frame += ev[0].elapsed_time(ev[1])
@@ -126,6 +126,15 @@ def test_stream21_480p(lay, torch, companion):
     q, k, v every pass, state carried across frames from S0 = 0."""
     w = SI.WORKLOADS["stream21_480p"]
     w = SI.companion(w) if companion else w
+    recs, out_errs, _ = _stream(lay, torch, w)
+    assert len(recs) == 21 and all(r["gpu_finite"] and r["ref_finite"] for r in recs)
+    _check(recs, out_errs, w.name)
+
+
+def test_stream21_480p_elementwise_gate(lay, torch):
+    """The 21-frame stream with the ablation's elementwise forget gate (one
+    value per d_k row, alpha = sigmoid(N(2, 0.5)) per element)."""
+    w = SI.scaled(SI.WORKLOADS["stream21_480p"], gate="elementwise", name="stream21_480p_elementwise")
     recs, out_errs, _ = _stream(lay, torch, w)
     assert len(recs) == 21 and all(r["gpu_finite"] and r["ref_finite"] for r in recs)
     _check(recs, out_errs, w.name)

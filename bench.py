@@ -219,6 +219,86 @@ def per_frame_report(path):
     return 0
 
 
+def stack_report(path, frames, layers=30, ratios=(0.0, 0.5, 0.75), pool=4):
+    """An attention-only stack: `layers` self-attention layers per pass, of
+    which round(ratio * layers) are this layer and the rest full-softmax
+    attention over their own key/value cache (the clean keys/values of every
+    previous frame, then the pass's own), for 4 query-only + 1 clean passes
+    per latent frame. Activations are synthetic and cycled from a small pool
+    (the work does not depend on the values). Per frame: GPU time of all
+    layers and passes (HIP events around the frame) and allocated device
+    memory after the frame."""
+    import torch
+
+    import synth_inputs as SI
+    from hybrid_softmax_gated_amd.layer import ARL2Layer, softmax_attention
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = SI.scaled(SI.companion(SI.WORKLOADS["stream21_480p"]), frames=pool)
+    B, H, d, L = w.B, w.H, w.d, w.L
+    npass = w.passes_per_frame
+    Wd = torch.from_numpy(SI.make_weights(w)).to(dev).to(torch.bfloat16)
+    inputs = list(SI.iter_passes_device(w, dev))  # pool x passes_per_frame
+    out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    base_alloc = torch.cuda.memory_allocated()
+    res = {"layers": layers, "frames": frames, "passes_per_frame": npass, "runs": {}}
+    for ratio in ratios:
+        n_arl2 = int(round(ratio * layers))
+        arl2 = [ARL2Layer(B, H, d, L, 0) for _ in range(n_arl2)]
+        ncache = layers - n_arl2
+        caps = [1] * ncache
+        kcs = [torch.empty((B, L, H, d), dtype=torch.bfloat16, device=dev) for _ in range(ncache)]
+        vcs = [torch.empty_like(k) for k in kcs]
+        run = {"arl2_layers": n_arl2, "softmax_layers": ncache, "ms": [], "allocated": []}
+        for f in range(frames):
+            for c in range(ncache):  # room for this frame's keys/values
+                if f + 1 > caps[c]:
+                    caps[c] *= 2
+                    k2 = torch.empty((B, caps[c] * L, H, d), dtype=torch.bfloat16, device=dev)
+                    v2 = torch.empty_like(k2)
+                    k2[:, :f * L] = kcs[c][:, :f * L]
+                    v2[:, :f * L] = vcs[c][:, :f * L]
+                    kcs[c], vcs[c] = k2, v2
+                    del k2, v2
+            torch.cuda.synchronize()
+            ev[0].record()
+            for ps in range(npass):
+                for li in range(layers):
+                    p = inputs[((f + li) % pool) * npass + ps]
+                    if li < n_arl2:
+                        arl2[li].forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update)
+                    else:
+                        c = li - n_arl2
+                        kcs[c][:, f * L:(f + 1) * L] = p.k
+                        vcs[c][:, f * L:(f + 1) * L] = p.v
+                        softmax_attention(p.q, kcs[c][:, :(f + 1) * L], vcs[c][:, :(f + 1) * L],
+                                          out, 0)
+            ev[1].record()
+            torch.cuda.synchronize()
+            run["ms"].append(ev[0].elapsed_time(ev[1]))
+            run["allocated"].append(torch.cuda.memory_allocated() - base_alloc)
+            if f % 25 == 0 or f == frames - 1:
+                print(f"stack {int(ratio * 100)}% frame {f + 1}: {run['ms'][-1]:.2f} ms, "
+                      f"{run['allocated'][-1] / 1e9:.2f} GB", file=sys.stderr, flush=True)
+        res["runs"][f"{int(ratio * 100)}%"] = run
+        del arl2, kcs, vcs
+        torch.cuda.empty_cache()
+    with open(path, "w") as fh:
+        json.dump(res, fh)
+    summ = {"metric": f"attention-only stack of {layers} layers, per-frame GPU ms and allocated "
+                      f"GB vs latent frame ({npass - 1} query-only + 1 clean passes, 12 heads, "
+                      f"d=128, L=1560)", "frames": frames}
+    for k, r in res["runs"].items():
+        pick = sorted({0, 20, 80, 230, frames - 1} & set(range(frames)))
+        summ[k] = {"ms": {i + 1: round(r["ms"][i], 3) for i in pick},
+                   "allocated_gb": {i + 1: round(r["allocated"][i] / 1e9, 3) for i in pick},
+                   "total_s": round(sum(r["ms"]) / 1e3, 3)}
+    print(json.dumps(summ), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +309,12 @@ def main() -> int:
     ap.add_argument("--gate", default="headwise", choices=["headwise", "elementwise"],
                     help="forget gate: one scalar per head (the method's) or one value per "
                          "d_k row (the ablation's)")
+    ap.add_argument("--stack-report", metavar="PATH", default="",
+                    help="instead of the throughput line: an attention-only stack of 30 layers "
+                         "in which 0, 50 and 75 %% of the softmax KV-cache layers are replaced by "
+                         "this layer, run over --stack-frames latent frames of 4 query-only + 1 "
+                         "clean passes; writes per-frame GPU time and device memory to PATH")
+    ap.add_argument("--stack-frames", type=int, default=252)
     ap.add_argument("--per-frame-report", metavar="PATH", default="",
                     help="instead of the throughput line: run the 231-frame long-horizon "
                          "schedule through the layer and through full-softmax attention over a "
@@ -260,6 +346,8 @@ def main() -> int:
         return 2
     if args.per_frame_report:
         return per_frame_report(args.per_frame_report)
+    if args.stack_report:
+        return stack_report(args.stack_report, args.stack_frames)
 
     import numpy as np
     import torch

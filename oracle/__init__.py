@@ -8,6 +8,7 @@ from .arl2_oracle import (  # noqa: F401
     delta_update,
     feature_map,
     frame_forward,
+    gate_projections,
     gate_state,
     head_forward,
     inter_read,
@@ -16,5 +17,6 @@ from .arl2_oracle import (  # noqa: F401
     l2_normalize_rows,
     output_rows,
     row_softmax,
+    sigmoid,
     token_level_update,
 )

@@ -144,6 +144,29 @@ def token_level_update(S: np.ndarray, Kp: np.ndarray, Vp: np.ndarray, alpha: flo
     return S
 
 
+# ------------------------------------------------------------ gates
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def gate_projections(x: np.ndarray, Wa: np.ndarray, Wb: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """The gates from the layer's token inputs ([TS] section 2.1: the gates
+    are learned per-token projections; [TS] section 4 and [AS] "Surprising
+    findings": the forget gate is headwise).
+
+    x [B][L][D] (the tokens entering the layer), Wa, Wb [D][H] -> alpha [B][H],
+    beta [B][L][H]. beta is one learning rate per token and head:
+    sigmoid(x_i . Wb[:, h]). The pages do not say how the per-token
+    projections become one forget gate per head and frame; the reading here
+    is the plainest pooling, the mean over the frame's tokens of the logits:
+    alpha[b][h] = sigmoid(mean_i x_i . Wa[:, h]). No bias.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    za = x @ np.asarray(Wa, dtype=np.float64)   # [B][L][H]
+    zb = x @ np.asarray(Wb, dtype=np.float64)
+    return sigmoid(za.mean(axis=1)), sigmoid(zb)
+
+
 # ------------------------------------------------------------ one layer
 def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, Wq: np.ndarray,
                  Wk: np.ndarray, Wv: np.ndarray, S: np.ndarray, alpha,

@@ -259,6 +259,45 @@ def SI_scaled_elementwise():
     return SI.Workload("gate", 2, 3, 16, 20, 1, 0, SI.F32, 0.0, seed=4, gate="elementwise")
 
 
+# ------------------------------------------------------------ gate projections
+def test_gate_projections_worked_example():
+    """x = [[1, 0], [0, 2]] (two tokens, D = 2), one head, Wa = [0.5, -1],
+    Wb = [2, 1]: the alpha logits of the tokens are 0.5 and -2 (mean -0.75),
+    the beta logits 2 and 2."""
+    x = np.array([[[1.0, 0.0], [0.0, 2.0]]])
+    Wa = np.array([[0.5], [-1.0]])
+    Wb = np.array([[2.0], [1.0]])
+    a, b = O.gate_projections(x, Wa, Wb)
+    assert a.shape == (1, 1) and b.shape == (1, 2, 1)
+    assert abs(a[0, 0] - 1.0 / (1.0 + math.exp(0.75))) < 1e-15
+    assert np.allclose(b[0, :, 0], 1.0 / (1.0 + math.exp(-2.0)), rtol=0, atol=1e-15)
+
+
+def test_gate_projections_invariants():
+    r = _rng(41)
+    B, L, D, H = 2, 9, 12, 3
+    x = r.normal(size=(B, L, D))
+    Wa, Wb = r.normal(size=(D, H)), r.normal(size=(D, H))
+    a, b = O.gate_projections(x, Wa, Wb)
+    # beta of a token depends on that token only
+    x2 = x.copy()
+    x2[:, 4] += 1.0
+    _, b2 = O.gate_projections(x2, Wa, Wb)
+    assert np.array_equal(np.delete(b2, 4, axis=1), np.delete(b, 4, axis=1))
+    # alpha is invariant to the order of the frame's tokens
+    perm = r.permutation(L)
+    a3, b3 = O.gate_projections(x[:, perm], Wa, Wb)
+    assert np.allclose(a3, a, rtol=0, atol=1e-14) and np.array_equal(b3, b[:, perm])
+    # sign symmetry of the logistic gate: sigmoid(-z) = 1 - sigmoid(z)
+    a4, b4 = O.gate_projections(-x, Wa, Wb)
+    assert np.allclose(a4, 1 - a, atol=1e-14) and np.allclose(b4, 1 - b, atol=1e-14)
+    # identical tokens: the pooled gate is the per-token gate of that token
+    xs = np.repeat(x[:, :1], L, axis=1)
+    a5, _ = O.gate_projections(xs, Wa, Wb)
+    _, b5 = O.gate_projections(xs, Wb=Wa, Wa=Wa)
+    assert np.allclose(a5, b5[:, 0], atol=1e-14)
+
+
 # ------------------------------------------------------------ P6: gradient
 def test_update_is_one_gradient_step_autograd():
     torch = pytest.importorskip("torch")
@@ -447,6 +486,11 @@ def _planted_variants():
     def l2_missing(x, eps=1e-6):
         return x
 
+    def gate_pooled_after_sigmoid(x, Wa, Wb):  # mean of the gates instead of the logits
+        x = np.asarray(x, dtype=np.float64)
+        return (O.sigmoid(x @ np.asarray(Wa, np.float64)).mean(axis=1),
+                O.sigmoid(x @ np.asarray(Wb, np.float64)))
+
     def gate_on_columns(S, alpha):            # elementwise gate scales d_v, not d_k
         a = np.asarray(alpha, dtype=np.float64)
         return float(a) * S if a.ndim == 0 else S * a[None, :]
@@ -461,6 +505,7 @@ def _planted_variants():
         "feature map transposed": ("feature_map", fmap_transposed),
         "L2 normalisation dropped": ("l2_normalize_rows", l2_missing),
         "elementwise gate on the wrong axis": ("gate_state", gate_on_columns),
+        "forget gate pooled after the sigmoid": ("gate_projections", gate_pooled_after_sigmoid),
     }
 
 
@@ -468,7 +513,8 @@ def _pin_suite():
     """The pins above that are sensitive to the planted slips."""
     return [test_worked_example_d2_state_and_read, test_update_is_one_gradient_step_autograd,
             test_consistent_memory_only_decays, test_single_token_general_gates,
-            test_token_permutation_equivariance, test_elementwise_gate_single_token_by_loops]
+            test_token_permutation_equivariance, test_elementwise_gate_single_token_by_loops,
+            test_gate_projections_worked_example]
 
 
 @pytest.mark.parametrize("label", list(_planted_variants().keys()))

@@ -299,6 +299,55 @@ def stack_report(path, frames, layers=30, ratios=(0.0, 0.5, 0.75), pool=4):
     return 0
 
 
+def gate_projection_leg(w, dev, stream, steps, repeat):
+    """Per-call GPU time of the gate projections (alpha and beta from the layer
+    input x [B][L][D], D = H*d, weights [H][D]) on the workload's shape,
+    against the HBM roofline: x, both weights and the gates are moved once.
+
+    The call is two short launches; issued from the host one by one, they
+    finish faster than the host enqueues them, so the time is taken from a
+    HIP graph of `repeat` calls replayed `steps` times (events on the
+    replay stream), and every replay's gates are checked against the eager
+    call's."""
+    import torch
+
+    import synth_inputs as SI
+    from hybrid_softmax_gated_amd import binding as Bd
+    from hybrid_softmax_gated_amd.layer import gate_projections
+
+    B, L, D, H = w.B, w.L, w.H * w.d, w.H
+    x, Wa, Wb = (torch.from_numpy(t).to(dev).to(torch.bfloat16)
+                 for t in SI.make_gate_inputs(B, L, D, H, SI.BF16, w.seed))
+    alpha, beta, ws = gate_projections(x, Wa, Wb, Bd.ARL2_BF16, stream=stream)
+    torch.cuda.synchronize()
+    a_ref, b_ref = alpha.clone(), beta.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for _ in range(repeat):
+            gate_projections(x, Wa, Wb, Bd.ARL2_BF16, alpha, beta, ws, cap)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = 0.0
+    for _ in range(steps):
+        alpha.zero_()
+        beta.zero_()
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms += e0.elapsed_time(e1)
+        assert torch.equal(alpha, a_ref) and torch.equal(beta, b_ref), "graph replay differs"
+    us = 1000.0 * ms / (steps * repeat)
+    nbytes = B * L * D * 2 + 2 * H * D * 2 + B * L * H * 4 + B * H * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "avg_call_us": round(us, 2), "bytes_per_call": nbytes,
+            "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "shape": f"x [{B}][{L}][{D}] bf16, Wa/Wb [{H}][{D}]",
+            "timing": f"HIP graph of {repeat} calls (2 launches each), {steps} replays"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,6 +373,9 @@ def main() -> int:
     ap.add_argument("--profile-repeat", type=int, default=10,
                     help="back-to-back launches of each idempotent kernel per event pair "
                          "in the per-kernel timing leg")
+    ap.add_argument("--gate-projections-only", action="store_true",
+                    help="only time the gate projections on the workload's shape and print "
+                         "their JSON object")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB 10 times (scales the HBM byte "
@@ -363,6 +415,11 @@ def main() -> int:
     if args.gate != "headwise":
         w = SI.scaled(w, name=f"{w.name}_{args.gate}_gate")
     B, H, d, L = w.B, w.H, w.d, w.L
+
+    if args.gate_projections_only:
+        leg = gate_projection_leg(w, dev, torch.cuda.current_stream(), 20, 50)
+        print(json.dumps({"workload": w.name, "gate_projections": leg}), flush=True)
+        return 0
 
     # ---- inputs, resident in HBM before timing
     W = SI.make_weights(w)
@@ -411,6 +468,8 @@ def main() -> int:
     Bd.arl2_profile_enable(False)
     kern_us = {k: 1000.0 * ms / n for k, (n, ms) in rep.items() if n}
 
+    gate_leg = gate_projection_leg(w, dev, stream, 20, 50)
+
     fa, fb, fc = flops(B, H, d, L)
     passes = w.passes_per_frame
     frame_flops = passes * (fa + fb) + fc
@@ -438,6 +497,7 @@ def main() -> int:
         "event_ms_per_step": round(ev_ms / args.steps, 5),
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": roofline,
+        "gate_projections": gate_leg,
     }
     if not args.no_cpu_baseline:
         host = []

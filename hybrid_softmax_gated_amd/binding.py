@@ -72,6 +72,8 @@ def _load() -> ctypes.CDLL:
                                          P]),
         "arl2_softmax_attention_workspace_bytes": (Z, [I, I, I, I, I, I]),
         "arl2_softmax_attention": (I, [P, P, P, I, I, I, I, I, I, P, P, Z, P]),
+        "arl2_gate_projections_workspace_bytes": (Z, [I, I, I, I, I]),
+        "arl2_gate_projections": (I, [P, P, P, I, I, I, I, I, P, P, P, Z, P]),
         "arl2_profile_enable": (I, [I, I]),
         "arl2_profile_report": (I, [ctypes.c_char_p, Z]),
         "arl2_profile_reset": (None, []),
@@ -88,6 +90,7 @@ _lib = _load()
 EXPORTED = ("arl2_version", "arl2_status_string", "arl2_last_error", "arl2_workspace_bytes",
             "arl2_state_init", "arl2_state_reset", "arl2_frame_forward", "arl2_frame_forward_gated",
             "arl2_softmax_attention_workspace_bytes", "arl2_softmax_attention",
+            "arl2_gate_projections_workspace_bytes", "arl2_gate_projections",
             "arl2_profile_enable", "arl2_profile_report", "arl2_profile_reset")
 
 
@@ -167,6 +170,16 @@ def arl2_softmax_attention(q, kc, vc, B: int, H: int, d: int, Lq: int, Lk: int, 
                            ws, ws_bytes: int, stream=None) -> None:
     _check(_lib.arl2_softmax_attention(_ptr(q), _ptr(kc), _ptr(vc), B, H, d, Lq, Lk, dtype,
                                        _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def arl2_gate_projections_workspace_bytes(B: int, L: int, D: int, H: int, dtype: int) -> int:
+    return int(_lib.arl2_gate_projections_workspace_bytes(B, L, D, H, dtype))
+
+
+def arl2_gate_projections(x, Wa, Wb, B: int, L: int, D: int, H: int, dtype: int, alpha, beta, ws,
+                          ws_bytes: int, stream=None) -> None:
+    _check(_lib.arl2_gate_projections(_ptr(x), _ptr(Wa), _ptr(Wb), B, L, D, H, dtype, _ptr(alpha),
+                                      _ptr(beta), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def arl2_profile_enable(on: bool, repeat: int = 1) -> None:

@@ -488,6 +488,71 @@ arl2_status arl2_softmax_attention(const void *q, const void *kc, const void *vc
   return ok();
 }
 
+static arl2_status check_gate_shape(int64_t B, int64_t L, int64_t D, int64_t H, int64_t dtype,
+                                    const char *what) {
+  if (dtype != ARL2_BF16 && dtype != ARL2_F32)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: dtype %lld is not ARL2_BF16 or ARL2_F32", what,
+                (long long)dtype);
+  if (B < 1 || B > kMaxB || L < 1 || L > ARL2_MAX_L || D < 1 || D > ARL2_MAX_GATE_D || H < 1 ||
+      H > kMaxH)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: bad shape B=%lld L=%lld D=%lld H=%lld", what,
+                (long long)B, (long long)L, (long long)D, (long long)H);
+  if (B * L * D > ((int64_t)1 << 40) || B * L * H > ((int64_t)1 << 36))
+    return fail(ARL2_ERR_INVALID_ARG, "%s: B=%lld L=%lld D=%lld H=%lld is too large", what,
+                (long long)B, (long long)L, (long long)D, (long long)H);
+  return ARL2_OK;
+}
+
+size_t arl2_gate_projections_workspace_bytes(int32_t B, int32_t L, int32_t D, int32_t H,
+                                             int32_t dtype) {
+  if (check_gate_shape(B, L, D, H, dtype, "arl2_gate_projections_workspace_bytes") != ARL2_OK)
+    return 0;
+  return arl2::plan_gate(B, L, D, H, dtype).ws_bytes;
+}
+
+arl2_status arl2_gate_projections(const void *x, const void *Wa, const void *Wb, int32_t B,
+                                  int32_t L, int32_t D, int32_t H, int32_t dtype, float *alpha,
+                                  float *beta, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "arl2_gate_projections";
+  arl2_status cs = check_gate_shape(B, L, D, H, dtype, fn);
+  if (cs != ARL2_OK) return cs;
+  const void *tens[3] = {x, Wa, Wb};
+  const char *names[3] = {"x", "Wa", "Wb"};
+  for (int i = 0; i < 3; ++i) {
+    if (!tens[i]) return fail(ARL2_ERR_INVALID_ARG, "%s: %s is NULL", fn, names[i]);
+    if (!aligned(tens[i], 16))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  if (!alpha || !beta || !aligned(alpha, 4) || !aligned(beta, 4))
+    return fail(ARL2_ERR_INVALID_ARG, "%s: alpha/beta are NULL or misaligned", fn);
+  const arl2::GatePlan gp = arl2::plan_gate(B, L, D, H, dtype);
+  const size_t need = gp.ws_bytes;
+  if (ws_bytes < need)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: workspace of %zu bytes, need %zu", fn, ws_bytes, need);
+  if (!ws || !aligned(ws, 256))
+    return fail(ARL2_ERR_INVALID_ARG, "%s: ws is NULL or not 256-byte aligned", fn);
+  const size_t es = esize(dtype);
+  const Range r_in[3] = {range(x, (size_t)B * L * D * es), range(Wa, (size_t)H * D * es),
+                         range(Wb, (size_t)H * D * es)};
+  const Range r_out[3] = {range(alpha, (size_t)B * H * 4), range(beta, (size_t)B * L * H * 4),
+                          range(ws, ws_bytes)};
+  const char *onames[3] = {"alpha", "beta", "ws"};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 3; ++i)
+      if (overlap(r_out[o], r_in[i]))
+        return fail(ARL2_ERR_INVALID_ARG, "%s: %s overlaps %s", fn, onames[o], names[i]);
+    for (int j = 0; j < o; ++j)
+      if (overlap(r_out[o], r_out[j]))
+        return fail(ARL2_ERR_INVALID_ARG, "%s: %s overlaps %s", fn, onames[o], onames[j]);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const arl2::GateArgs ga{x, Wa, Wb, B, L, D, H, dtype, gp, ws, alpha, beta};
+  hipError_t e;
+  if ((e = timed("gate_projections", s, [&] { return arl2::launch_gate_projections(ga, s); })))
+    return hip_status(e, fn);
+  return ok();
+}
+
 arl2_status arl2_profile_enable(int32_t on, int32_t repeat) {
   if (repeat < 1 || repeat > 1000)
     return fail(ARL2_ERR_INVALID_ARG, "arl2_profile_enable: repeat %d not in [1, 1000]", repeat);

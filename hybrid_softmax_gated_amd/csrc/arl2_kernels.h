@@ -81,6 +81,28 @@ hipError_t launch_delta_apply(float *S, const float *alpha, bool elementwise, co
 // dst[i] := src ? src[i] : 0 for i < n.
 hipError_t launch_fill_state(float *dst, const float *src, int64_t n, hipStream_t s);
 
+// ---------------------------------------------------------------- gate projections
+// Z = x [Wa; Wb]^T on the matrix cores (bf16, D a multiple of 64) or with
+// VALU dot products (generic path); beta is written directly, alpha after a
+// second launch sums the per-tile alpha logits.
+struct GatePlan {
+  bool mfma = false;
+  int ntt = 0, nnt = 0;  // 16-token tiles, 32-column tiles
+  int nta = 0;           // alpha partials per stream (token tiles, or tokens)
+  size_t ws_bytes = 0;   // alpha partials [B][nta][H] fp32
+};
+GatePlan plan_gate(int64_t B, int64_t L, int64_t D, int64_t H, int dtype);
+
+struct GateArgs {
+  const void *x;          // [B][L][D]
+  const void *Wa, *Wb;    // [H][D]
+  int B, L, D, H, dtype;
+  GatePlan plan;
+  void *ws;               // plan.ws_bytes, 256-byte aligned
+  float *alpha, *beta;    // [B][H], [B][L][H]
+};
+hipError_t launch_gate_projections(const GateArgs &a, hipStream_t s);
+
 // ---------------------------------------------------------------- generic path
 // Any dtype, d in {16, 128}: plain VALU kernels for the small fp32 workloads.
 // dtype: 0 = bf16, 1 = f32 (arl2_dtype).

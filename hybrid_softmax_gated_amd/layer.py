@@ -48,3 +48,22 @@ def softmax_attention(q, kc, vc, out, dtype: int, ws=None, stream=None):
         ws = torch.empty(nb, dtype=torch.uint8, device=q.device)
     B.arl2_softmax_attention(q, kc, vc, Bn, H, d, Lq, Lk, dtype, out, ws, nb, stream)
     return ws
+
+
+def gate_projections(x, Wa, Wb, dtype: int, alpha=None, beta=None, ws=None, stream=None):
+    """alpha [B][H] and beta [B][L][H] (fp32) from the layer input x [B][L][D]
+    and the gate weights Wa, Wb [H][D]; allocates what is not given with
+    torch. Returns (alpha, beta, ws)."""
+    Bn, L, D = x.shape
+    H = Wa.shape[0]
+    nb = B.arl2_gate_projections_workspace_bytes(Bn, L, D, H, dtype)
+    if nb == 0:
+        raise ValueError(f"invalid gate projection shape B={Bn} L={L} D={D} H={H}")
+    if ws is None or ws.numel() < nb:
+        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    if alpha is None:
+        alpha = torch.empty((Bn, H), dtype=torch.float32, device=x.device)
+    if beta is None:
+        beta = torch.empty((Bn, L, H), dtype=torch.float32, device=x.device)
+    B.arl2_gate_projections(x, Wa, Wb, Bn, L, D, H, dtype, alpha, beta, ws, nb, stream)
+    return alpha, beta, ws

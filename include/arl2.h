@@ -183,6 +183,38 @@ ARL2_API arl2_status arl2_softmax_attention(const void *q, const void *kc, const
                                    void *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Gate projections: the delta rule's gates computed from the tokens that
+ * enter the layer ("Technical Summary ...", section 2.1: alpha and beta are
+ * learned per-token projections; section 4, ablations: the forget gate is
+ * headwise). With z_a = x . Wa[h] and z_b = x . Wb[h] per token:
+ *   beta[b][t][h] = sigmoid(x[b][t] . Wb[h])          one per token and head
+ *   alpha[b][h]   = sigmoid(mean_t x[b][t] . Wa[h])   one per stream, head, frame
+ * The pages do not state how per-token forget gates become the one headwise
+ * gate a frame-level update applies; this library pools the logits by their
+ * mean over the frame's L tokens. No bias. The outputs are laid out as the
+ * alpha and beta arguments of arl2_frame_forward take them.
+ *   x      device [B][L][D] in `dtype`: the frame's tokens entering the layer
+ *   Wa, Wb device [H][D] in `dtype`: one row of D weights per head (the
+ *          weight layout of a linear map from D to H features)
+ *   alpha  device [B][H] float32 (written)
+ *   beta   device [B][L][H] float32 (written)
+ *   ws     device workspace of arl2_gate_projections_workspace_bytes(...)
+ *          bytes, 256-byte aligned; contents need not be initialised.
+ * Sums are in fp32; bf16 inputs with D a multiple of 64 use the matrix cores.
+ * Errors: INVALID_ARG for a bad dtype or shape (B, L, H >= 1, 1 <= D <=
+ * ARL2_MAX_GATE_D), NULL or misaligned pointers (x, Wa, Wb 16 bytes; alpha,
+ * beta 4 bytes), a short workspace, or outputs that overlap the inputs or
+ * each other. The workspace-size query returns 0 for a bad shape.
+ */
+#define ARL2_MAX_GATE_D (1 << 16)
+ARL2_API size_t arl2_gate_projections_workspace_bytes(int32_t B, int32_t L, int32_t D, int32_t H,
+                                                      int32_t dtype);
+ARL2_API arl2_status arl2_gate_projections(const void *x, const void *Wa, const void *Wb,
+                                           int32_t B, int32_t L, int32_t D, int32_t H,
+                                           int32_t dtype, float *alpha, float *beta, void *ws,
+                                           size_t ws_bytes, void *stream);
+
+/*
  * Kernel timing (diagnostics). While enabled, every kernel the library
  * launches is bracketed by a pair of hipEvents recorded on the launch stream.
  * A kernel that only reads its inputs and overwrites its outputs (all but

@@ -16,6 +16,10 @@ Workload recipe (the pages give the model shape, not the activations):
   frame, d_k row) for elementwise gating), beta = sigmoid(N(0, 1)) per
   (stream, token, head, frame), fp32.
 * S0 = 0, or N(0, 0.02) per element where a workload asks for a warm state.
+* Gate projections (``make_gate_inputs``): layer input x [B][L][D] =
+  mu_b + N(0, 1) per element with a per-stream channel mean mu_b ~ N(0, 0.5),
+  so that the frame-pooled logits are not all near zero; weights Wa, Wb
+  [H][D] ~ N(0, 1/D), so the logits are of order one.
 * For bf16 workloads every io tensor (q, k, v, W) is drawn in float32 and
   rounded to bfloat16 with round-to-nearest-even; the float32 arrays returned
   here hold exactly the bf16 values, and ``bits`` arrays hold the raw bf16
@@ -38,6 +42,7 @@ F32 = "f32"
 _TAG_W = 11
 _TAG_S0 = 12
 _TAG_STREAM = 13
+_TAG_GATE = 14
 
 
 # ---------------------------------------------------------------- bf16 bytes
@@ -202,6 +207,17 @@ def random_pass(B: int, H: int, d: int, L: int, dtype: str, seed: int,
     pi = next(iter_passes(w))
     pi.update = update
     return pi
+
+
+def make_gate_inputs(B: int, L: int, D: int, H: int, dtype: str, seed: int):
+    """(x [B][L][D], Wa [H][D], Wb [H][D]) as io-dtype values in float32."""
+    rng = np.random.default_rng([_TAG_GATE, seed])
+    mu = rng.standard_normal((B, 1, D), dtype=np.float32) * np.float32(0.5)
+    x = mu + rng.standard_normal((B, L, D), dtype=np.float32)
+    sd = np.float32(1.0 / np.sqrt(D))
+    Wa = rng.standard_normal((H, D), dtype=np.float32) * sd
+    Wb = rng.standard_normal((H, D), dtype=np.float32) * sd
+    return _store(x, dtype), _store(Wa, dtype), _store(Wb, dtype)
 
 
 # ------------------------------------------------------- device-side drawing

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert {"arl2_state_init", "arl2_state_reset", "arl2_frame_forward",
             "arl2_frame_forward_gated", "arl2_workspace_bytes"} <= names
-    assert len(names) == 13
+    assert len(names) == 15
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -179,6 +179,36 @@ def test_softmax_attention_validation(B):
     assert _code(B.arl2_softmax_attention, Q, K, V, 1, 12, 128, 1560, 4680, 0, OUT, None, nb)[0] == E
     assert _code(B.arl2_softmax_attention, Q, K, V, 1, 12, 128, 1560, 4680, 0, Q, FAKE_WS, nb)[0] == E
     assert _code(B.arl2_softmax_attention, Q, K, V, 1, 12, 48, 1560, 4680, 0, OUT, FAKE_WS, nb)[0] == B.ARL2_ERR_UNSUPPORTED
+
+
+def test_gate_projections_validation(B):
+    E = B.ARL2_ERR_INVALID_ARG
+    wsb = B.arl2_gate_projections_workspace_bytes
+    nb = wsb(1, 1560, 1536, 12, B.ARL2_BF16)
+    assert nb > 0 and nb % 256 == 0
+    assert wsb(1, 100, 48, 3, B.ARL2_F32) >= 100 * 3 * 4   # one alpha logit per token and head
+    for bad in [(0, 1560, 1536, 12, 0), (1, 0, 1536, 12, 0), (1, 1560, 0, 12, 0),
+                (1, 1560, 1536, 0, 0), (1, 1560, 1536, 12, 3), (1, 1560, (1 << 16) + 1, 12, 0)]:
+        assert wsb(*bad) == 0
+    X, WA, WB, A, BT = Q, K, V, AL, BE
+    g = B.arl2_gate_projections
+    args = [X, WA, WB, 1, 1560, 1536, 12, 0, A, BT, FAKE_WS, nb]
+    def call(**kw):
+        a = list(args)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return _code(g, *a)
+    assert call(a0=None)[0] == E                      # x NULL
+    assert call(a1=WA + 8)[0] == E                    # Wa misaligned
+    assert call(a8=None)[0] == E                      # alpha NULL
+    assert call(a9=BT + 2)[0] == E                    # beta misaligned
+    assert "workspace" in call(a11=nb - 1)[1]
+    assert call(a10=FAKE_WS + 16)[0] == E             # ws misaligned
+    assert call(a8=X + 64)[0] == E                    # alpha inside x
+    assert call(a9=A)[0] == E                         # beta overlaps alpha
+    assert call(a10=BT)[0] == E                       # workspace overlaps beta
+    assert call(a7=9)[0] == E                         # dtype
+    assert call(a4=0)[0] == E                         # L
 
 
 def test_binding_refuses_to_load_without_the_library(repo_root):

@@ -18,5 +18,7 @@ from .arl2_oracle import (  # noqa: F401
     output_rows,
     row_softmax,
     sigmoid,
+    token_level_frame_forward,
+    token_level_head_forward,
     token_level_update,
 )

@@ -20,7 +20,8 @@ Where the pages leave a step open this module takes the plainest reading and
 says so in the function's docstring (softmax scale, no mask, row-vector
 feature maps without bias, the L2 normalisation of Q' and K' with a 1e-6
 floor, the transpose of K' in the update, the plain sum of the branches,
-headwise-scalar alpha and per-token beta).
+headwise-scalar alpha and per-token beta, and for the token-level ablation
+the read of each token after its own write).
 
 Arrays are float64; inputs that were stored in bfloat16 or float32 widen to
 float64 exactly, so the oracle sees the same values as the GPU.
@@ -142,6 +143,62 @@ def token_level_update(S: np.ndarray, Kp: np.ndarray, Vp: np.ndarray, alpha: flo
         a = alpha if i == 0 else 1.0
         S = a * S + beta[i] * np.outer(k, Vp[i] - k @ S)
     return S
+
+
+def token_level_head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, Wq: np.ndarray,
+                             Wk: np.ndarray, Wv: np.ndarray, S: np.ndarray, alpha: float,
+                             beta: np.ndarray, update: bool) -> Tuple[np.ndarray, np.ndarray]:
+    """One pass of one head with token-level access, the ablation that
+    frame-level access is compared with ([TS] section 4, [AS] "Surprising
+    findings"; [TS] section 2.2 describes the frame-level design it departs
+    from).
+
+    The pages name the ablation and report worse quality, nothing more. The
+    reading here: inside the frame the tokens write the state one after
+    another (``token_level_update``), and token i's query reads the state
+    right after its own write, O_inter[i] = q'_i S_i, the order of the Gated
+    Delta Network recurrence the method builds on ([AS] "Builds on"). The
+    intra branch and the plain sum are unchanged. Clean-pass updates still
+    hold: on a noisy pass the within-frame states only serve the reads and
+    are dropped; on the clean pass S_L becomes S_N. alpha and beta are used
+    on every pass. Returns (out, S_next).
+    """
+    o_intra = intra_attention(q, k, v)
+    Qp = l2_normalize_rows(feature_map(q, Wq))
+    Kp = l2_normalize_rows(feature_map(k, Wk))
+    Vp = feature_map(v, Wv)
+    o_inter = np.empty_like(o_intra)
+    Si = S
+    for i in range(Kp.shape[0]):
+        a = alpha if i == 0 else 1.0
+        Si = token_level_update(Si, Kp[i:i + 1], Vp[i:i + 1], a, beta[i:i + 1])
+        o_inter[i] = Qp[i] @ Si
+    return o_intra + o_inter, (Si if update else S)
+
+
+def token_level_frame_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, Wphi: np.ndarray,
+                              S: np.ndarray, alpha, beta, update_flag: int) -> np.ndarray:
+    """``frame_forward`` with token-level access (``token_level_head_forward``
+    per stream and head). alpha [B][H] and beta [B][L][H] are required on
+    every pass. S [B][H][d][d] is updated in place on the clean pass."""
+    assert update_flag in (0, 1)
+    B, L, H, d = q.shape
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    W = np.asarray(Wphi, dtype=np.float64)
+    out = np.empty((B, L, H, d), dtype=np.float64)
+    new_states = {}
+    for b in range(B):
+        for h in range(H):
+            o, s_next = token_level_head_forward(
+                q[b, :, h], k[b, :, h], v[b, :, h], W[0, h], W[1, h], W[2, h], S[b, h],
+                float(alpha[b][h]), np.asarray(beta[b][:, h], dtype=np.float64),
+                bool(update_flag))
+            out[b, :, h] = o
+            if update_flag:
+                new_states[(b, h)] = s_next
+    for (b, h), s_next in new_states.items():
+        S[b, h] = s_next
+    return out
 
 
 # ------------------------------------------------------------ gates

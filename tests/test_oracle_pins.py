@@ -349,6 +349,90 @@ def test_frame_level_differs_from_token_level_except_single_token():
     np.testing.assert_allclose(fr1, tk1, rtol=1e-14, atol=1e-14)
 
 
+def _tl_identity_weights(d):
+    return np.eye(d), np.eye(d), np.eye(d)
+
+
+def test_token_level_worked_example_d2():
+    """d = 2, two tokens, identity feature maps. Keys e1, e2, values
+    (2, 3), (5, 7), queries e1, e2, S0 = I, alpha = 0.5, beta = (1, 0.5).
+    Token 1 (gate applied, residual against S0):
+      S_1 = 0.5 I + e1 ((2, 3) - (1, 0)) = [[1.5, 3], [0, 0.5]],  o_1 = e1 S_1 = (1.5, 3).
+    Token 2 (residual against S_1):
+      S_2 = S_1 + 0.5 e2 ((5, 7) - (0, 0.5)) = [[1.5, 3], [2.5, 3.75]],  o_2 = (2.5, 3.75).
+    Frame-level access on the same inputs reads S0 and ends at
+      0.5 I + [[1, 3], [0, 0]] + 0.5 [[0, 0], [5, 6]] = [[1.5, 3], [2.5, 3.5]]."""
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    k = q.copy()
+    v = np.array([[2.0, 3.0], [5.0, 7.0]])
+    Wq, Wk, Wv = _tl_identity_weights(2)
+    S0 = np.eye(2)
+    beta = np.array([1.0, 0.5])
+    out, S2 = O.token_level_head_forward(q, k, v, Wq, Wk, Wv, S0, 0.5, beta, True)
+    o_inter = out - O.intra_attention(q, k, v)
+    np.testing.assert_allclose(o_inter, [[1.5, 3.0], [2.5, 3.75]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S2, [[1.5, 3.0], [2.5, 3.75]], rtol=0, atol=1e-14)
+    _, Sf = O.head_forward(q, k, v, Wq, Wk, Wv, S0, 0.5, beta, True)
+    np.testing.assert_allclose(Sf, [[1.5, 3.0], [2.5, 3.5]], rtol=0, atol=1e-14)
+
+
+def test_token_level_orthonormal_keys_store_exactly():
+    """S0 = 0, beta = 1 and orthonormal keys: every write stores its value
+    exactly, so S_i = sum_{j <= i} k_j v_j^T and o_i = q'_i S_i."""
+    r = _rng(61)
+    d, L = 8, 5
+    Qk, _ = np.linalg.qr(r.normal(size=(d, d)))
+    k = Qk[:L]
+    q = r.normal(size=(L, d))
+    v = r.normal(size=(L, d))
+    Wq, Wk, Wv = _tl_identity_weights(d)
+    out, S = O.token_level_head_forward(q, k, v, Wq, Wk, Wv, np.zeros((d, d)), 0.7,
+                                        np.ones(L), True)
+    qn = q / np.linalg.norm(q, axis=1, keepdims=True)
+    expect = np.stack([qn[i] @ (k[:i + 1].T @ v[:i + 1]) for i in range(L)])
+    np.testing.assert_allclose(out - O.intra_attention(q, k, v), expect, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S, k.T @ v, rtol=0, atol=1e-12)
+
+
+def test_token_level_special_cases():
+    q, k, v, W, S, alpha, beta = _head_case(71)
+    # alpha = 1, beta = 0: nothing is written, so both accesses read S
+    o_t, S_t = O.token_level_head_forward(q, k, v, *W, S, 1.0, np.zeros_like(beta), True)
+    o_f, _ = O.head_forward(q, k, v, *W, S, 1.0, np.zeros_like(beta), False)
+    np.testing.assert_allclose(o_t, o_f, rtol=0, atol=1e-13)
+    assert np.array_equal(S_t, S)
+    # one token: the state is the frame-level state and the read sees it
+    o1, S1 = O.token_level_head_forward(q[:1], k[:1], v[:1], *W, S, alpha, beta[:1], True)
+    _, Sf1 = O.head_forward(q[:1], k[:1], v[:1], *W, S, alpha, beta[:1], True)
+    np.testing.assert_allclose(S1, Sf1, rtol=0, atol=1e-13)
+    Qp = O.l2_normalize_rows(O.feature_map(q[:1], W[0]))
+    np.testing.assert_allclose(o1 - O.intra_attention(q[:1], k[:1], v[:1]), Qp @ Sf1,
+                               rtol=0, atol=1e-13)
+    # a noisy pass reads the within-frame states but leaves S as it was
+    o_n, S_n = O.token_level_head_forward(q, k, v, *W, S, alpha, beta, False)
+    o_c, S_c = O.token_level_head_forward(q, k, v, *W, S, alpha, beta, True)
+    assert S_n is S and np.array_equal(o_n, o_c) and not np.allclose(S_c, S)
+
+
+def test_token_level_frame_forward_per_stream_and_head():
+    r = _rng(81)
+    B, L, H, d = 2, 6, 3, 4
+    q, k, v = (r.normal(size=(B, L, H, d)) for _ in range(3))
+    W = np.eye(d)[None, None] + 0.1 * r.normal(size=(3, H, d, d))
+    S = r.normal(size=(B, H, d, d))
+    alpha = r.uniform(0.5, 1.0, size=(B, H))
+    beta = r.uniform(0.0, 1.0, size=(B, L, H))
+    S_ref = S.copy()
+    out = O.token_level_frame_forward(q, k, v, W, S, alpha, beta, 1)
+    for b in range(B):
+        for h in range(H):
+            o, s = O.token_level_head_forward(q[b, :, h], k[b, :, h], v[b, :, h], W[0, h],
+                                              W[1, h], W[2, h], S_ref[b, h], alpha[b, h],
+                                              beta[b, :, h], True)
+            np.testing.assert_array_equal(out[b, :, h], o)
+            np.testing.assert_array_equal(S[b, h], s)
+
+
 # ------------------------------------------------------------ P10: growth rate
 def test_state_growth_equals_spectral_radius_of_transition():
     """With V' = 0 the frame update is S -> (alpha I - K'^T diag(beta) K') S;
@@ -491,6 +575,23 @@ def _planted_variants():
         return (O.sigmoid(x @ np.asarray(Wa, np.float64)).mean(axis=1),
                 O.sigmoid(x @ np.asarray(Wb, np.float64)))
 
+    def _tl(read_first, gate_all):
+        def f(q, k, v, Wq, Wk, Wv, S, alpha, beta, update):
+            Qp = O.l2_normalize_rows(O.feature_map(q, Wq))
+            Kp = O.l2_normalize_rows(O.feature_map(k, Wk))
+            Vp = O.feature_map(v, Wv)
+            o = np.empty_like(Qp)
+            Si = S
+            for i in range(Kp.shape[0]):
+                if read_first:
+                    o[i] = Qp[i] @ Si
+                a = alpha if (i == 0 or gate_all) else 1.0
+                Si = O.token_level_update(Si, Kp[i:i + 1], Vp[i:i + 1], a, beta[i:i + 1])
+                if not read_first:
+                    o[i] = Qp[i] @ Si
+            return O.intra_attention(q, k, v) + o, (Si if update else S)
+        return f
+
     def gate_on_columns(S, alpha):            # elementwise gate scales d_v, not d_k
         a = np.asarray(alpha, dtype=np.float64)
         return float(a) * S if a.ndim == 0 else S * a[None, :]
@@ -506,6 +607,9 @@ def _planted_variants():
         "L2 normalisation dropped": ("l2_normalize_rows", l2_missing),
         "elementwise gate on the wrong axis": ("gate_state", gate_on_columns),
         "forget gate pooled after the sigmoid": ("gate_projections", gate_pooled_after_sigmoid),
+        "token-level read before its own write": ("token_level_head_forward",
+                                                  _tl(True, False)),
+        "token-level forget gate at every token": ("token_level_head_forward", _tl(False, True)),
     }
 
 
@@ -514,7 +618,7 @@ def _pin_suite():
     return [test_worked_example_d2_state_and_read, test_update_is_one_gradient_step_autograd,
             test_consistent_memory_only_decays, test_single_token_general_gates,
             test_token_permutation_equivariance, test_elementwise_gate_single_token_by_loops,
-            test_gate_projections_worked_example]
+            test_gate_projections_worked_example, test_token_level_worked_example_d2]
 
 
 @pytest.mark.parametrize("label", list(_planted_variants().keys()))

@@ -70,12 +70,13 @@ def measured_traffic(kernel, workload, digest):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(frames_host, W, w, budget_s=15.0, max_frames=400):
+def cpu_baseline(frames_host, W, w, budget_s=15.0, max_frames=400, access="frame"):
     """Time the float64 oracle on host copies of the same frames. Workloads
     whose full frame would not fit the budget are timed on one (stream,
     head) of each pass and scaled by the number of (stream, head) pairs."""
     import numpy as np
     import oracle as O
+    fwd = O.token_level_frame_forward if access == "token" else O.frame_forward
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -90,11 +91,10 @@ def cpu_baseline(frames_host, W, w, budget_s=15.0, max_frames=400):
         for p in frames_host[done % len(frames_host)]:
             if one_head:
                 sl = (slice(0, 1), slice(None), slice(0, 1))
-                O.frame_forward(p["q"][sl], p["k"][sl], p["v"][sl], Wf[:, 0:1], S,
-                                p["alpha"][0:1, 0:1], p["beta"][0:1, :, 0:1], int(p["update"]))
+                fwd(p["q"][sl], p["k"][sl], p["v"][sl], Wf[:, 0:1], S, p["alpha"][0:1, 0:1],
+                    p["beta"][0:1, :, 0:1], int(p["update"]))
             else:
-                O.frame_forward(p["q"], p["k"], p["v"], Wf, S, p["alpha"], p["beta"],
-                                int(p["update"]))
+                fwd(p["q"], p["k"], p["v"], Wf, S, p["alpha"], p["beta"], int(p["update"]))
         done += 1
     dt = time.perf_counter() - t0
     scale = w.B * w.H if one_head else 1
@@ -358,6 +358,10 @@ def main() -> int:
     ap.add_argument("--gate", default="headwise", choices=["headwise", "elementwise"],
                     help="forget gate: one scalar per head (the method's) or one value per "
                          "d_k row (the ablation's)")
+    ap.add_argument("--access", default="frame", choices=["frame", "token"],
+                    help="state access: frame-level (the method's) or token-level (the "
+                         "ablation's: tokens write the state in turn, each reading it after "
+                         "its own write)")
     ap.add_argument("--stack-report", metavar="PATH", default="",
                     help="instead of the throughput line: an attention-only stack of 30 layers "
                          "in which 0, 50 and 75 %% of the softmax KV-cache layers are replaced by "
@@ -414,6 +418,11 @@ def main() -> int:
     w = SI.scaled(SI.companion(SI.WORKLOADS[args.workload]), gate=args.gate)
     if args.gate != "headwise":
         w = SI.scaled(w, name=f"{w.name}_{args.gate}_gate")
+    if args.access == "token":
+        if args.gate != "headwise":
+            print("bench.py: token-level access takes the headwise gate", file=sys.stderr)
+            return 2
+        w = SI.scaled(w, name=f"{w.name}_token_level")
     B, H, d, L = w.B, w.H, w.d, w.L
 
     if args.gate_projections_only:
@@ -438,7 +447,12 @@ def main() -> int:
 
     def step(i):
         for p in frames[i % len(frames)]:
-            layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, stream, gate=w.gate)
+            if args.access == "token":
+                layer.forward_token_level(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update,
+                                          stream)
+            else:
+                layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, stream,
+                              gate=w.gate)
 
     for i in range(args.warmup):
         step(i)
@@ -505,7 +519,7 @@ def main() -> int:
             host.append([{"q": p.q.float().cpu().numpy(), "k": p.k.float().cpu().numpy(),
                           "v": p.v.float().cpu().numpy(), "alpha": p.alpha.cpu().numpy(),
                           "beta": p.beta.cpu().numpy(), "update": p.update} for p in fr])
-        res["cpu_baseline"] = cpu_baseline(host, W, w)
+        res["cpu_baseline"] = cpu_baseline(host, W, w, access=args.access)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -70,6 +70,9 @@ def _load() -> ctypes.CDLL:
         "arl2_frame_forward": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, P, P, I, P]),
         "arl2_frame_forward_gated": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, I, P, P, I,
                                          P]),
+        "arl2_token_level_workspace_bytes": (Z, [I, I, I, I, I]),
+        "arl2_frame_forward_token_level": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, P, P, I,
+                                               P, Z, P]),
         "arl2_softmax_attention_workspace_bytes": (Z, [I, I, I, I, I, I]),
         "arl2_softmax_attention": (I, [P, P, P, I, I, I, I, I, I, P, P, Z, P]),
         "arl2_gate_projections_workspace_bytes": (Z, [I, I, I, I, I]),
@@ -91,6 +94,7 @@ EXPORTED = ("arl2_version", "arl2_status_string", "arl2_last_error", "arl2_works
             "arl2_state_init", "arl2_state_reset", "arl2_frame_forward", "arl2_frame_forward_gated",
             "arl2_softmax_attention_workspace_bytes", "arl2_softmax_attention",
             "arl2_gate_projections_workspace_bytes", "arl2_gate_projections",
+            "arl2_token_level_workspace_bytes", "arl2_frame_forward_token_level",
             "arl2_profile_enable", "arl2_profile_report", "arl2_profile_reset")
 
 
@@ -159,6 +163,18 @@ def arl2_frame_forward_gated(q, k, v, Wphi, st: arl2_state, alpha, gate: int, be
     _check(_lib.arl2_frame_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(Wphi), ctypes.byref(st),
                                          _ptr(alpha), gate, _ptr(beta), _ptr(out), update_flag,
                                          _stream(stream)))
+
+
+def arl2_token_level_workspace_bytes(B: int, H: int, d: int, L: int, dtype: int) -> int:
+    return int(_lib.arl2_token_level_workspace_bytes(B, H, d, L, dtype))
+
+
+def arl2_frame_forward_token_level(q, k, v, Wphi, st: arl2_state, alpha, beta, out,
+                                   update_flag: int, tl_ws, tl_ws_bytes: int, stream=None) -> None:
+    _check(_lib.arl2_frame_forward_token_level(_ptr(q), _ptr(k), _ptr(v), _ptr(Wphi),
+                                               ctypes.byref(st), _ptr(alpha), _ptr(beta),
+                                               _ptr(out), update_flag, _ptr(tl_ws), tl_ws_bytes,
+                                               _stream(stream)))
 
 
 def arl2_softmax_attention_workspace_bytes(B: int, H: int, d: int, Lq: int, Lk: int,

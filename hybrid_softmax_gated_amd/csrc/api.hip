@@ -423,6 +423,114 @@ arl2_status arl2_frame_forward_gated(const void *q, const void *k, const void *v
                             out, update_flag, stream);
 }
 
+namespace {
+
+// Token-level workspace: chunk records, then O_inter (MFMA path only).
+struct TokenPlan {
+  size_t off_oi = 0, total = 0;
+};
+TokenPlan plan_token(int64_t B, int64_t H, int64_t d, int64_t L, int32_t dtype) {
+  TokenPlan tp;
+  if (!mfma_path((int32_t)d, dtype)) return tp;
+  const int64_t nchunk = (L + arl2::kTokenChunk - 1) / arl2::kTokenChunk;
+  tp.off_oi = align256((size_t)B * H * nchunk * arl2::kTokenRecordBytes);
+  tp.total = tp.off_oi + align256((size_t)B * L * H * d * sizeof(float));
+  return tp;
+}
+
+}  // namespace
+
+size_t arl2_token_level_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t L,
+                                        int32_t dtype) {
+  if (check_shape(B, H, d, L, dtype, "arl2_token_level_workspace_bytes") != ARL2_OK) return 0;
+  return plan_token(B, H, d, L, dtype).total;
+}
+
+arl2_status arl2_frame_forward_token_level(const void *q, const void *k, const void *v,
+                                           const void *Wphi, arl2_state *st, const float *alpha,
+                                           const float *beta, void *out, int32_t update_flag,
+                                           void *tl_ws, size_t tl_ws_bytes, void *stream) {
+  const char *fn = "arl2_frame_forward_token_level";
+  arl2_status cs = check_state(st, fn);
+  if (cs != ARL2_OK) return cs;
+  if (update_flag != 0 && update_flag != 1)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: update_flag %d is not 0 or 1", fn, update_flag);
+  const void *tens[5] = {q, k, v, Wphi, out};
+  const char *names[5] = {"q", "k", "v", "Wphi", "out"};
+  for (int i = 0; i < 5; ++i) {
+    if (!tens[i]) return fail(ARL2_ERR_INVALID_ARG, "%s: %s is NULL", fn, names[i]);
+    if (!aligned(tens[i], 16))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  if (!alpha || !beta || !aligned(alpha, 4) || !aligned(beta, 4))
+    return fail(ARL2_ERR_INVALID_ARG, "%s: alpha and beta are required on every pass", fn);
+  const int64_t B = st->B, H = st->H, d = st->d, L = st->L;
+  const TokenPlan tp = plan_token(B, H, d, L, st->dtype);
+  if (tl_ws_bytes < tp.total)
+    return fail(ARL2_ERR_INVALID_ARG, "%s: token-level workspace of %zu bytes, need %zu", fn,
+                tl_ws_bytes, tp.total);
+  if (tp.total > 0 && (!tl_ws || !aligned(tl_ws, 256)))
+    return fail(ARL2_ERR_INVALID_ARG, "%s: tl_ws is NULL or not 256-byte aligned", fn);
+  const size_t es = esize(st->dtype);
+  const size_t act = (size_t)B * L * H * d * es;
+  const Range r_out = range(out, act), r_S = range(st->S, (size_t)B * H * d * d * 4),
+              r_ws = range(st->ws, st->ws_bytes),
+              r_tl = tp.total ? range(tl_ws, tl_ws_bytes) : Range{0, 0};
+  const Range r_in[6] = {range(q, act), range(k, act), range(v, act),
+                         range(Wphi, (size_t)3 * H * d * d * es), range(alpha, (size_t)B * H * 4),
+                         range(beta, (size_t)B * L * H * 4)};
+  const char *in_names[6] = {"q", "k", "v", "Wphi", "alpha", "beta"};
+  const Range r_w[4] = {r_out, r_S, r_ws, r_tl};
+  const char *w_names[4] = {"out", "the state", "the state's workspace", "tl_ws"};
+  for (int a = 0; a < 4; ++a) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(r_w[a], r_in[i]))
+        return fail(ARL2_ERR_INVALID_ARG, "%s: %s overlaps %s", fn, w_names[a], in_names[i]);
+    for (int c = 0; c < a; ++c)
+      if (overlap(r_w[a], r_w[c]))
+        return fail(ARL2_ERR_INVALID_ARG, "%s: %s overlaps %s", fn, w_names[a], w_names[c]);
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const FramePlan fp = plan_frame(B, H, d, L, st->dtype);
+  char *ws = (char *)st->ws;
+  float *ws_o = (float *)(ws + fp.off_o);
+  float *ws_ml = (float *)(ws + fp.off_ml);
+  const char *wbase = (const char *)Wphi;
+  const void *Wq = wbase;
+  const void *Wk = wbase + (size_t)H * d * d * es;
+  const void *Wv = wbase + (size_t)2 * H * d * d * es;
+  const int iB = (int)B, iH = (int)H, iL = (int)L, id = (int)d, dt = st->dtype;
+  float *S = st->S;
+  hipError_t e;
+  if (fp.mfma) {
+    float *o_inter = (float *)((char *)tl_ws + tp.off_oi);
+    const arl2::AttnArgs aa{q, k, v, iB, iH, iL, iL, fp.ap, ws_o, ws_ml};
+    const arl2::TokenLevelArgs ta{q, k, v, Wq, Wk, Wv, alpha, beta, S, iB, iH, iL, update_flag,
+                                  tl_ws, o_inter};
+    arl2::CombineArgs ca{ws_o, ws_ml, q, nullptr, nullptr, iB, iH, iL, fp.ap, out};
+    ca.o_inter = o_inter;
+    if ((e = timed("attn_partial", s, [&] { return arl2::launch_attn_partial_bf16(aa, s); })))
+      return hip_status(e, fn);
+    if ((e = timed("token_level", s, [&] { return arl2::launch_token_level_bf16(ta, s); },
+                   /*idempotent=*/update_flag == 0)))
+      return hip_status(e, fn);
+    if ((e = timed("combine_token_level", s, [&] { return arl2::launch_tail_bf16(ca, nullptr, s); })))
+      return hip_status(e, fn);
+  } else {
+    if ((e = timed("generic_attention", s, [&] {
+           return arl2::launch_generic_attention(dt, id, q, k, v, iB, iH, iL, iL, ws_o, s);
+         })))
+      return hip_status(e, fn);
+    if ((e = timed("generic_token_level", s, [&] {
+           return arl2::launch_token_level_generic(dt, id, q, k, v, Wphi, ws_o, S, alpha, beta,
+                                                   iB, iH, iL, update_flag, out, s);
+         }, /*idempotent=*/update_flag == 0)))
+      return hip_status(e, fn);
+  }
+  return ok();
+}
+
 size_t arl2_softmax_attention_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t Lq,
                                               int32_t Lk, int32_t dtype) {
   if (check_shape(B, H, d, Lq, dtype, "arl2_softmax_attention_workspace_bytes") != ARL2_OK ||

@@ -56,6 +56,7 @@ struct CombineArgs {
   int B, H, L;
   AttnPlan plan;
   void *out;  // [B][L][H][128] bf16
+  const float *o_inter = nullptr;  // [B][L][H][128] fp32, added instead of the read when set
 };
 
 // Chunk contributions dS_c of the gated delta update (clean pass).
@@ -80,6 +81,27 @@ hipError_t launch_delta_apply(float *S, const float *alpha, bool elementwise, co
                               int B, int H, int d, int nchunk, hipStream_t s);
 // dst[i] := src ? src[i] : 0 for i < n.
 hipError_t launch_fill_state(float *dst, const float *src, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- token-level access
+constexpr int kTokenChunk = 64;            // tokens per chunk of the recurrence
+constexpr int kTokenRecordBytes = 122880;  // MFMA operands of one chunk
+struct TokenLevelArgs {
+  const void *q, *k, *v;          // [B][L][H][128] bf16
+  const void *Wq, *Wk, *Wv;       // [H][128][128] bf16
+  const float *alpha, *beta;      // [B][H], [B][L][H]
+  float *S;                       // [B][H][128][128], written when update
+  int B, H, L, update;
+  void *records;                  // [B][H][nchunk] x kTokenRecordBytes
+  float *o_inter;                 // [B][L][H][128] fp32
+};
+// Chunk operands, then the in-order recurrence: O_inter and (update) S.
+hipError_t launch_token_level_bf16(const TokenLevelArgs &a, hipStream_t s);
+// Any dtype, d in {16, 128}: out = o_intra + O_inter token by token, where
+// o_intra is [B][H][L][d] fp32 (the generic attention's layout).
+hipError_t launch_token_level_generic(int dtype, int d, const void *q, const void *k,
+                                      const void *v, const void *W, const float *o_intra,
+                                      float *S, const float *alpha, const float *beta, int B,
+                                      int H, int L, int update, void *out, hipStream_t s);
 
 // ---------------------------------------------------------------- gate projections
 // Z = x [Wa; Wb]^T on the matrix cores (bf16, D a multiple of 64) or with

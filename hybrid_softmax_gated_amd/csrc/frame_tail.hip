@@ -57,6 +57,7 @@ struct CombineKParams {
   const float *S;
   int H, L, nqblk, nsplit, nitems;
   bf16 *out;
+  const float *o_inter;  // [B][L][H][128] fp32, added when set (and Wq null)
 };
 
 // out = (sum_s w_s Ohat_s) / (sum_s w_s) + O_inter with w_s = 2^(m_s - M) l_s,
@@ -170,6 +171,18 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) acc[bb] = mfma32(sa[bb], qb, acc[bb]);
     }
+  } else if (p.o_inter) {
+    // A precomputed inter-frame term, in the accumulators' order: register
+    // 4r + e of block bb is feature 32bb + 8r + 4(l/32) + e.
+    const float *oi = p.o_inter + ((int64_t)b * p.L + qrow) * tok + (int64_t)h * D + 4 * hl;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 x = qrow < p.L ? *(const f32x4 *)(oi + 32 * bb + 8 * r) : zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[bb][4 * r + e] = x[e];
+      }
   } else {
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) acc[bb] = zero16();
@@ -527,6 +540,7 @@ hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_
   P.c.nsplit = c.plan.nsplit;
   P.c.nitems = c.B * c.H * c.plan.nqblk;
   P.c.out = (bf16 *)c.out;
+  P.c.o_inter = c.Wq ? nullptr : c.o_inter;
   P.per_xcd_c = (P.c.nitems + 7) / 8;
   P.d = DeltaKParams{};
   P.delta_blocks = 0;

@@ -37,6 +37,18 @@ class ARL2Layer:
             B.arl2_frame_forward_gated(q, k, v, W, self.st, alpha, B.ARL2_GATE_ELEMENTWISE, beta,
                                        out, 1 if update else 0, stream)
 
+    def forward_token_level(self, q, k, v, W, alpha, beta, out, update: bool,
+                            stream=None) -> None:
+        """One pass with token-level access: each token writes S in turn and
+        reads it after its own write. The extra workspace is allocated once."""
+        Bn, H, d, L = self.shape
+        nb = B.arl2_token_level_workspace_bytes(Bn, H, d, L, self.dtype)
+        if nb and (getattr(self, "tl_ws", None) is None or self.tl_ws.numel() < nb):
+            self.tl_ws = torch.empty(nb, dtype=torch.uint8, device=self.S.device)
+        B.arl2_frame_forward_token_level(q, k, v, W, self.st, alpha, beta, out,
+                                         1 if update else 0, self.tl_ws if nb else None, nb,
+                                         stream)
+
 
 def softmax_attention(q, kc, vc, out, dtype: int, ws=None, stream=None):
     """Full-softmax attention over a key/value cache (the comparator);

@@ -169,6 +169,36 @@ ARL2_API arl2_status arl2_frame_forward_gated(const void *q, const void *k, cons
                                      int32_t update_flag, void *stream);
 
 /*
+ * One pass with token-level state access: the ablation that frame-level
+ * access is compared with ("Technical Summary ...", section 4; frame-level
+ * access is section 2.2). The pages only name it; the reading here: inside
+ * the frame the tokens write the state one after another and each token's
+ * query reads it right after its own write,
+ *   S_1 = alpha S_0 + beta_1 k'_1 (v'_1 - k'_1^T S_0),
+ *   S_i = S_{i-1} + beta_i k'_i (v'_i - k'_i^T S_{i-1})  (i > 1),
+ *   out[i] = O_intra[i] + q'_i S_i,
+ * with the forget gate applied once per frame, with the first token (a
+ * one-token frame is the frame-level update). Clean-pass updates still hold:
+ * update_flag = 0 forms the within-frame states for the reads only and
+ * leaves S bitwise unchanged; update_flag = 1 stores S_L.
+ * Arguments as for arl2_frame_forward (headwise alpha [B][H]), except:
+ *   alpha, beta  required on every pass;
+ *   tl_ws        device workspace of arl2_token_level_workspace_bytes(...)
+ *                bytes, 256-byte aligned, contents need not be initialised
+ *                (the size is 0, and tl_ws may be NULL, for shapes other than
+ *                bf16 with d = 128, which run token by token).
+ * Errors: as arl2_frame_forward, plus INVALID_ARG for NULL alpha/beta, a
+ * short or misaligned tl_ws, or tl_ws overlapping any other buffer.
+ */
+ARL2_API size_t arl2_token_level_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t L,
+                                                 int32_t dtype);
+ARL2_API arl2_status arl2_frame_forward_token_level(const void *q, const void *k, const void *v,
+                                                    const void *Wphi, arl2_state *st,
+                                                    const float *alpha, const float *beta,
+                                                    void *out, int32_t update_flag, void *tl_ws,
+                                                    size_t tl_ws_bytes, void *stream);
+
+/*
  * Full-softmax attention of Lq queries over Lk cached keys/values per stream
  * and head, with scale 1/sqrt(d) and no mask: the growing key/value-cache
  * attention that the method replaces ("Technical Summary ...", section 1,

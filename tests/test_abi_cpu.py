@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert {"arl2_state_init", "arl2_state_reset", "arl2_frame_forward",
             "arl2_frame_forward_gated", "arl2_workspace_bytes"} <= names
-    assert len(names) == 15
+    assert len(names) == 17
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -209,6 +209,25 @@ def test_gate_projections_validation(B):
     assert call(a10=BT)[0] == E                       # workspace overlaps beta
     assert call(a7=9)[0] == E                         # dtype
     assert call(a4=0)[0] == E                         # L
+
+
+def test_token_level_validation(B):
+    E = B.ARL2_ERR_INVALID_ARG
+    st = _fake_state(B)
+    nb = B.arl2_token_level_workspace_bytes(1, 2, 128, 100, 0)
+    assert nb > 0 and nb % 256 == 0
+    assert B.arl2_token_level_workspace_bytes(1, 2, 16, 100, 1) == 0   # token-by-token kernel
+    assert B.arl2_token_level_workspace_bytes(1, 2, 64, 100, 0) == 0   # unsupported d
+    TL = 0x7F2000000000
+    f = B.arl2_frame_forward_token_level
+    assert _code(f, Q, K, V, W, st, None, BE, OUT, 0, TL, nb)[0] == E      # alpha on every pass
+    assert _code(f, Q, K, V, W, st, AL, None, OUT, 1, TL, nb)[0] == E
+    assert "workspace" in _code(f, Q, K, V, W, st, AL, BE, OUT, 1, TL, nb - 1)[1]
+    assert _code(f, Q, K, V, W, st, AL, BE, OUT, 1, None, nb)[0] == E
+    assert _code(f, Q, K, V, W, st, AL, BE, OUT, 1, TL + 16, nb)[0] == E
+    assert _code(f, Q, K, V, W, st, AL, BE, OUT, 1, FAKE_WS, nb)[0] == E   # overlaps the state's ws
+    assert _code(f, Q, K, V, W, st, AL, BE, OUT, 1, OUT, nb)[0] == E       # overlaps out
+    assert _code(f, Q, K, V, W, st, AL, BE, OUT, 2, TL, nb)[0] == E
 
 
 def test_binding_refuses_to_load_without_the_library(repo_root):

@@ -45,12 +45,14 @@ constexpr int NSL = D / 16;      // 16-column state slices per head
 constexpr int VROW = D + 4;      // padded fp32 row of a token vector in LDS
 constexpr int GROW = TC + 4;     // padded fp32 row of a chunk's Gram matrix
 
-// Chunk record (one per stream, head and chunk), all MFMA-ready:
-//   W   [wave 4][lane 64][row tile 4]     bf16x8 hi, bf16x8 lo  (A of W S)
-//   Q   [wave 4][lane 64][row tile 4]     bf16x8                (A of Q S)
-//   KT  [wave 4][lane 64][tile 2][kstep 2] bf16x8 hi, lo       (A of K^T R)
-//   M   [row tile 4][lane 64][kstep 2]    bf16x8                (A of M R)
-//   U   [row tile 4][slice 8][lane 64]    f32x4                 (R layout)
+// Chunk record (one per stream, head and chunk), all MFMA-ready, 16 bytes
+// per lane with the lane index fastest, so that each wavefront load or store
+// covers 1 KB of consecutive bytes:
+//   W   [wave 4][row tile 4][hi, lo][lane 64]    bf16x8  (A of W S)
+//   Q   [wave 4][row tile 4][lane 64]            bf16x8  (A of Q S)
+//   KT  [wave 4][tile 2][kstep 2][hi, lo][lane]  bf16x8  (A of K^T R)
+//   M   [row tile 4][kstep 2][lane 64]           bf16x8  (A of M R)
+//   U   [row tile 4][slice 8][lane 64]           f32x4   (R layout)
 constexpr int OFF_W = 0;
 constexpr int OFF_Q = OFF_W + 4 * 64 * 4 * 32;
 constexpr int OFF_KT = OFF_Q + 4 * 64 * 4 * 16;
@@ -86,9 +88,14 @@ struct PrepParams {
   char *rec;                   // [B][H][nchunk] records
 };
 
-__global__ __launch_bounds__(256) void tl_prep_kernel(PrepParams p) {
+// Eight wavefronts. (A) waves 0-5 each project one 32-token tile of one map
+// (k, v, q); (B) waves 0-5 each form one 32x32 tile of K K^T or Q K^T while
+// waves 6-7 write the Q and K^T records; (C) waves 0-3 run the forward
+// substitution (one column per lane) while waves 4-7 write the M record;
+// (D) everyone writes the W and U records.
+__global__ __launch_bounds__(512) void tl_prep_kernel(PrepParams p) {
   __shared__ __attribute__((aligned(16))) float vecs[3][TC][VROW];  // Q', K', V' (then W, U)
-  __shared__ __attribute__((aligned(16))) float gram[2][TC][GROW];  // K K^T, Q K^T
+  __shared__ __attribute__((aligned(16))) float gram[2][TC][GROW];  // beta-scaled K K^T, Q K^T
   __shared__ float betas[TC], bgs[TC];
   const int bid = blockIdx.x;
   const int item = (bid & 7) * p.per_xcd + (bid >> 3);
@@ -98,6 +105,7 @@ __global__ __launch_bounds__(256) void tl_prep_kernel(PrepParams p) {
   const int h = bh % p.H, b = bh / p.H;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, r16 = lane & 15;
   const int t0 = chunk * TC;
   const int nvalid = min(TC, p.L - t0);
   const int tokB = p.H * D * 2;
@@ -112,8 +120,8 @@ __global__ __launch_bounds__(256) void tl_prep_kernel(PrepParams p) {
 #pragma unroll
     for (int m = 0; m < 3; ++m)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int cc = 8 * wave + i, row = 4 * cc + r4;
+      for (int i = 0; i < 4; ++i) {
+        const int cc = 4 * wave + i, row = 4 * cc + r4;
         global_to_lds16(Ws[m] + row * D + 8 * (pos ^ tile_swz(row & 15)),
                         tiles + m * 32768 + cc * 1024);
       }
@@ -123,158 +131,169 @@ __global__ __launch_bounds__(256) void tl_prep_kernel(PrepParams p) {
     betas[tid] = bt;
     bgs[tid] = (chunk == 0 && tid > 0) ? bt * alpha : bt;
   }
-  // Jobs: round 0 maps k (waves 0, 1) and v (waves 2, 3) of token tile
-  // wave & 1; round 1 maps q (waves 0, 1).
+  // Projection job of waves 0-5: map k, v, q for waves (0, 1), (2, 3),
+  // (4, 5); token tile wave & 1.
+  const bool proj = wave < 6;
   const int tt = wave & 1;
-  const int m0 = wave < 2 ? 1 : 2;
-  const uint32_t span = (uint32_t)nvalid * (uint32_t)tokB;
-  bf16x8 op0[8], op1[8];
-  {
-    const char *base = (const char *)((m0 == 1 ? p.k : p.v) + (((int64_t)b * p.L + t0) * p.H + h) * D);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, span);
+  const int m0 = wave < 2 ? 1 : wave < 4 ? 2 : 0;
+  bf16x8 op0[8];
+  if (proj) {
+    const bf16 *src = m0 == 1 ? p.k : m0 == 2 ? p.v : p.q;
+    const char *base = (const char *)(src + (((int64_t)b * p.L + t0) * p.H + h) * D);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)nvalid * (uint32_t)tokB);
 #pragma unroll
     for (int c = 0; c < 8; ++c) op0[c] = buffer_load16(r, (32 * tt + l32) * tokB + 32 * c + 16 * hl);
-  }
-  if (wave < 2) {
-    const char *base = (const char *)(p.q + (((int64_t)b * p.L + t0) * p.H + h) * D);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, span);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) op1[c] = buffer_load16(r, (32 * tt + l32) * tokB + 32 * c + 16 * hl);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // (x W)^T: rows = output features 32bb + 8(i/4) + 4(l/32) + i%4, column =
   // token 32 tt + l%32.
-  f32x16 a0[4], a1[4];
+  f32x16 a0[4];
+  float s0 = 1.f;
+  if (proj) {
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) a0[bb] = zero16();
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int k0 = 16 * c + 8 * hl;
-    bf16x8 wa[4];
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-      wa[bb] = tile_col_operand(tiles + m0 * 32768, k0, k0 + 4, lane, bb);
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) a0[bb] = mfma32(wa[bb], op0[c], a0[bb]);
-  }
-  if (wave < 2) {
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) a1[bb] = zero16();
+    for (int bb = 0; bb < 4; ++bb) a0[bb] = zero16();
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int k0 = 16 * c + 8 * hl;
       bf16x8 wa[4];
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) wa[bb] = tile_col_operand(tiles, k0, k0 + 4, lane, bb);
+      for (int bb = 0; bb < 4; ++bb)
+        wa[bb] = tile_col_operand(tiles + m0 * 32768, k0, k0 + 4, lane, bb);
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) a1[bb] = mfma32(wa[bb], op1[c], a1[bb]);
+      for (int bb = 0; bb < 4; ++bb) a0[bb] = mfma32(wa[bb], op0[c], a0[bb]);
+    }
+    if (m0 != 2) {
+      float ss = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss = fmaf(a0[bb][i], a0[bb][i], ss);
+      ss += swap_halves(ss);
+      s0 = 1.f / fmaxf(sqrtf(ss), kL2Eps);
     }
   }
-  auto inv_norm = [&](const f32x16 *a) {
-    float ss = 0.f;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ss = fmaf(a[bb][i], a[bb][i], ss);
-    ss += swap_halves(ss);
-    return 1.f / fmaxf(sqrtf(ss), kL2Eps);
-  };
-  const float s0 = m0 == 1 ? inv_norm(a0) : 1.f;
-  const float s1 = wave < 2 ? inv_norm(a1) : 1.f;
   __syncthreads();  // every wave is done with the weight tiles
-  {
+  if (proj) {
     const int tok = 32 * tt + l32;
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int f = 32 * bb + 8 * r + 4 * hl;
         f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = a0[bb][4 * r + e] * s0;
-        *(f32x4 *)&vecs[m0][tok][f] = x;
-        if (wave < 2) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = a1[bb][4 * r + e] * s1;
-          *(f32x4 *)&vecs[0][tok][f] = x;
-        }
+        *(f32x4 *)&vecs[m0][tok][32 * bb + 8 * r + 4 * hl] = x;
       }
   }
   __syncthreads();
 
-  // (B) K K^T and Q K^T on or below the diagonal, split bf16. Tile jobs
-  // (matrix, row block, column block): wave 0: G00 G10; wave 1: G11 P00;
-  // wave 2: P10; wave 3: P11. Rows of a tile are tokens 32rb + 8(i/4) +
-  // 4(l/32) + i%4, columns tokens 32cb + l%32.
-  {
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      if (jb == 1 && wave >= 2) break;
-      // (mat, rb, cb) of this wave's job jb, per the list above.
-      const int mat = wave == 0 ? 0 : wave == 1 ? jb : 1;
-      const int rb = wave == 0 ? jb : wave == 1 ? 1 - jb : 1;
-      const int cb = wave == 0 ? 0 : wave == 1 ? 1 - jb : wave - 2;
-      const float(*A)[VROW] = vecs[mat == 0 ? 1 : 0];
-      f32x16 acc = zero16();
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int f = 16 * st + 8 * hl;
-        float xa[8], xb[8];
-        *(f32x4 *)&xa[0] = *(const f32x4 *)&A[32 * rb + l32][f];
-        *(f32x4 *)&xa[4] = *(const f32x4 *)&A[32 * rb + l32][f + 4];
-        *(f32x4 *)&xb[0] = *(const f32x4 *)&vecs[1][32 * cb + l32][f];
-        *(f32x4 *)&xb[4] = *(const f32x4 *)&vecs[1][32 * cb + l32][f + 4];
-        bf16x8 ah, al, bh8, bl8;
-        split8(xa, ah, al);
-        split8(xb, bh8, bl8);
-        acc = mfma32(ah, bh8, acc);
-        acc = mfma32(ah, bl8, acc);
-        acc = mfma32(al, bh8, acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        gram[mat][32 * rb + 8 * (i >> 2) + 4 * hl + (i & 3)][32 * cb + l32] = acc[i];
-    }
-  }
-  // Q (plain bf16) and K^T (split) records, straight from the vectors.
   char *rec = p.rec + (int64_t)item * REC;
-  {
-    const int g = lane >> 4, r16 = lane & 15;
+  if (proj) {
+    // (B) tile `wave` of: G00 G10 G11 (K K^T) and P00 P10 P11 (Q K^T), split
+    // bf16. Rows are tokens 32rb + 8(i/4) + 4(l/32) + i%4, columns tokens
+    // 32cb + l%32.
+    const int mat = wave >= 3 ? 1 : 0, idx = wave % 3;
+    const int rb = idx == 0 ? 0 : 1, cb = idx == 2 ? 1 : 0;
+    const float(*A)[VROW] = vecs[mat == 0 ? 1 : 0];
+    f32x16 acc = zero16();
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const float *row = &vecs[0][16 * rt + r16][32 * wave + 4 * g];
-      bf16x8 qh;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qh[e] = (bf16)row[e];
-        qh[4 + e] = (bf16)row[16 + e];
-      }
-      *(bf16x8 *)(rec + OFF_Q + ((wave * 64 + lane) * 4 + rt) * 16) = qh;
+    for (int st = 0; st < 8; ++st) {
+      const int f = 16 * st + 8 * hl;
+      float xa[8], xb[8];
+      *(f32x4 *)&xa[0] = *(const f32x4 *)&A[32 * rb + l32][f];
+      *(f32x4 *)&xa[4] = *(const f32x4 *)&A[32 * rb + l32][f + 4];
+      *(f32x4 *)&xb[0] = *(const f32x4 *)&vecs[1][32 * cb + l32][f];
+      *(f32x4 *)&xb[4] = *(const f32x4 *)&vecs[1][32 * cb + l32][f + 4];
+      bf16x8 ah, al, bh8, bl8;
+      split8(xa, ah, al);
+      split8(xb, bh8, bl8);
+      acc = mfma32(ah, bh8, acc);
+      acc = mfma32(ah, bl8, acc);
+      acc = mfma32(al, bh8, acc);
     }
+    // P is stored as is; K K^T transposed and with column i scaled by
+    // beta_i, i.e. gram[0][j][i] = beta_i (k'_i . k'_j), the row the
+    // substitution below reads for token j.
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int i = 0; i < 16; ++i) {
+      const int ri = 32 * rb + 8 * (i >> 2) + 4 * hl + (i & 3), cj = 32 * cb + l32;
+      if (mat == 0)
+        gram[0][cj][ri] = betas[ri] * acc[i];
+      else
+        gram[1][ri][cj] = acc[i];
+    }
+  } else {
+    // Q (plain bf16) and K^T (split) records, straight from the vectors;
+    // waves 6 and 7 each take two of the four d_k blocks.
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        float x[8];
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int w = (wave - 6) + 2 * k2;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = vecs[1][32 * ks + pi32(g, e)][32 * wave + 16 * t + r16];
-        bf16x8 hi, lo;
-        split8(x, hi, lo);
-        char *dst = rec + OFF_KT + (((wave * 64 + lane) * 2 + t) * 2 + ks) * 32;
-        *(bf16x8 *)dst = hi;
-        *(bf16x8 *)(dst + 16) = lo;
+      for (int rt = 0; rt < 4; ++rt) {
+        const float *row = &vecs[0][16 * rt + r16][32 * w + 4 * g];
+        bf16x8 qh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qh[e] = (bf16)row[e];
+          qh[4 + e] = (bf16)row[16 + e];
+        }
+        *(bf16x8 *)(rec + OFF_Q + (w * 4 + rt) * 1024 + lane * 16) = qh;
       }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = vecs[1][32 * ks + pi32(g, e)][32 * w + 16 * t + r16];
+          bf16x8 hi, lo;
+          split8(x, hi, lo);
+          char *dst = rec + OFF_KT + ((w * 2 + t) * 2 + ks) * 2048 + lane * 16;
+          *(bf16x8 *)dst = hi;
+          *(bf16x8 *)(dst + 1024) = lo;
+        }
+    }
   }
   __syncthreads();
 
-  // (C) M = tril(Q K^T) (inclusive) record; then the forward substitution
-  // (I + tril(diag(beta) K K^T, -1)) X = [diag(beta g) K | diag(beta) V],
-  // one column of X per thread, rows in order.
-  {
-    const int g = lane >> 4, r16 = lane & 15;
-    const int rt = wave, i = 16 * rt + r16;
+  // (C) waves 0-3: the forward substitution
+  //   (I + tril(diag(beta) K K^T, -1)) X = [diag(beta g) K | diag(beta) V],
+  // one column of X per lane; waves 4-7: the M = tril(Q K^T) record.
+  if (wave < 4) {
+    const bool isK = tid < D;
+    const int col = isK ? tid : tid - D;
+    float(*X)[VROW] = vecs[isK ? 1 : 2];
+    // Column order: once x_j is final, every later row takes its term
+    // (x_i -= beta_i (k'_i . k'_j) x_j). Each step is up to 63 independent
+    // FMAs on one broadcast LDS row; row j + 1 is read while row j's FMAs
+    // run (two row buffers).
+    float x[TC];
+#pragma unroll
+    for (int i = 0; i < TC; ++i) x[i] = X[i][col] * (isK ? bgs[i] : betas[i]);
+    f32x4 row[2][TC / 4];
+#pragma unroll
+    for (int i4 = 0; i4 < TC; i4 += 4) row[0][i4 / 4] = *(const f32x4 *)&gram[0][0][i4];
+#pragma unroll
+    for (int j = 0; j < TC - 1; ++j) {
+      if (j + 1 < TC - 1) {
+#pragma unroll
+        for (int i4 = (j + 2) & ~3; i4 < TC; i4 += 4)
+          row[(j + 1) & 1][i4 / 4] = *(const f32x4 *)&gram[0][j + 1][i4];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i4 = (j + 1) & ~3; i4 < TC; i4 += 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i4 + e > j) x[i4 + e] = fmaf(-row[j & 1][i4 / 4][e], x[j], x[i4 + e]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TC; ++i) X[i][col] = x[i];
+  } else {
+    const int rt = wave - 4, i = 16 * rt + r16;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 mh;
@@ -283,60 +302,37 @@ __global__ __launch_bounds__(256) void tl_prep_kernel(PrepParams p) {
         const int j = 32 * ks + pi32(g, e);
         mh[e] = (bf16)(j <= i ? gram[1][i][j] : 0.f);
       }
-      *(bf16x8 *)(rec + OFF_M + ((rt * 64 + lane) * 2 + ks) * 16) = mh;
+      *(bf16x8 *)(rec + OFF_M + (rt * 2 + ks) * 1024 + lane * 16) = mh;
     }
-  }
-  {
-    const bool isK = tid < D;
-    const int col = isK ? tid : tid - D;
-    float(*X)[VROW] = vecs[isK ? 1 : 2];
-    float x[TC];
-#pragma unroll
-    for (int i = 0; i < TC; ++i) {
-      float s = 0.f;
-#pragma unroll
-      for (int j4 = 0; j4 < i; j4 += 4) {
-        const f32x4 gr = *(const f32x4 *)&gram[0][i][j4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (j4 + e < i) s = fmaf(gr[e], x[j4 + e], s);
-      }
-      const float rhs = X[i][col] * (isK ? bgs[i] : betas[i]);
-      x[i] = fmaf(-betas[i], s, rhs);
-    }
-#pragma unroll
-    for (int i = 0; i < TC; ++i) X[i][col] = x[i];
   }
   __syncthreads();
 
   // (D) W (split) and U records.
-  {
-    const int g = lane >> 4, r16 = lane & 15;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const float *row = &vecs[1][16 * rt + r16][32 * wave + 4 * g];
-      float x[8];
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int combo = 2 * wave + k2, w = combo >> 2, rt = combo & 3;
+    const float *row = &vecs[1][16 * rt + r16][32 * w + 4 * g];
+    float x[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = row[e];
-        x[4 + e] = row[16 + e];
-      }
-      bf16x8 hi, lo;
-      split8(x, hi, lo);
-      char *dst = rec + OFF_W + ((wave * 64 + lane) * 4 + rt) * 32;
-      *(bf16x8 *)dst = hi;
-      *(bf16x8 *)(dst + 16) = lo;
+    for (int e = 0; e < 4; ++e) {
+      x[e] = row[e];
+      x[4 + e] = row[16 + e];
     }
+    bf16x8 hi, lo;
+    split8(x, hi, lo);
+    char *dst = rec + OFF_W + (w * 4 + rt) * 2048 + lane * 16;
+    *(bf16x8 *)dst = hi;
+    *(bf16x8 *)(dst + 1024) = lo;
+  }
 #pragma unroll
-    for (int k2 = 0; k2 < 8; ++k2) {
-      const int unit = tid + 256 * k2;  // (rt, slice, lane)
-      const int ln = unit & 63, sl = (unit >> 6) & 7, rt = unit >> 9;
-      const int gg = ln >> 4, c = 16 * sl + (ln & 15);
-      f32x4 u;
+  for (int k2 = 0; k2 < 4; ++k2) {
+    const int unit = tid + 512 * k2;  // (rt, slice, lane)
+    const int ln = unit & 63, sl = (unit >> 6) & 7, rt = unit >> 9;
+    const int gg = ln >> 4, c = 16 * sl + (ln & 15);
+    f32x4 u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = vecs[2][16 * rt + 4 * gg + e][c];
-      *(f32x4 *)(rec + OFF_U + unit * 16) = u;
-    }
+    for (int e = 0; e < 4; ++e) u[e] = vecs[2][16 * rt + 4 * gg + e][c];
+    *(f32x4 *)(rec + OFF_U + unit * 16) = u;
   }
 }
 
@@ -365,33 +361,140 @@ struct ChunkOps {
 
 __device__ __forceinline__ void load_ops(ChunkOps &o, const char *rec, int wave, int lane,
                                          int slice) {
-  const char *w = rec + OFF_W + (wave * 64 + lane) * 4 * 32;
+  const char *w = rec + OFF_W + wave * 4 * 2048 + lane * 16;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    o.wh[rt] = *(const bf16x8 *)(w + rt * 32);
-    o.wl[rt] = *(const bf16x8 *)(w + rt * 32 + 16);
-    o.qh[rt] = *(const bf16x8 *)(rec + OFF_Q + ((wave * 64 + lane) * 4 + rt) * 16);
+    o.wh[rt] = *(const bf16x8 *)(w + rt * 2048);
+    o.wl[rt] = *(const bf16x8 *)(w + rt * 2048 + 1024);
+    o.qh[rt] = *(const bf16x8 *)(rec + OFF_Q + (wave * 4 + rt) * 1024 + lane * 16);
   }
-  const char *kt = rec + OFF_KT + (wave * 64 + lane) * 4 * 32;
+  const char *kt = rec + OFF_KT + wave * 4 * 2048 + lane * 16;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      o.kh[t][ks] = *(const bf16x8 *)(kt + (2 * t + ks) * 32);
-      o.kl[t][ks] = *(const bf16x8 *)(kt + (2 * t + ks) * 32 + 16);
+      o.kh[t][ks] = *(const bf16x8 *)(kt + (2 * t + ks) * 2048);
+      o.kl[t][ks] = *(const bf16x8 *)(kt + (2 * t + ks) * 2048 + 1024);
     }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
-    o.mh[ks] = *(const bf16x8 *)(rec + OFF_M + ((wave * 64 + lane) * 2 + ks) * 16);
+    o.mh[ks] = *(const bf16x8 *)(rec + OFF_M + (wave * 2 + ks) * 1024 + lane * 16);
   o.u = *(const f32x4 *)(rec + OFF_U + ((wave * NSL + slice) * 64 + lane) * 16);
+}
+
+struct RecurCtx {
+  f32x4 (*red)[2][4][4][64];  // [buf][R/O][wave][tile][lane]
+  bf16x8 (*rb)[4][64];         // [buf][tile][lane]: 4 hi, 4 lo
+  float *o_inter;
+  int H, L, b, h, slice, wave, lane, g, r16;
+  float alpha;
+};
+
+// One chunk: R = U - W S and Q S from the four waves' shares, then O and
+// S <- S' + K^T R (S' = alpha S for the frame's first chunk).
+__device__ __forceinline__ void recur_chunk(const RecurCtx &x, const ChunkOps &cur, int c,
+                                            f32x4 (&st)[2]) {
+  const int wave = x.wave, lane = x.lane, g = x.g, r16 = x.r16;
+  const float alpha = x.alpha;
+  auto &red = x.red;
+  auto &rb = x.rb;
+  const int buf = c & 1;
+  // S rows of this wave as a 32-deep B operand (k order pi32).
+  float sv[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sv[e] = st[0][e];
+    sv[4 + e] = st[1][e];
+  }
+  bf16x8 sh, sl;
+  split8(sv, sh, sl);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f32x4 pr = mfma16(cur.wh[rt], sh, zero4());
+    pr = mfma16(cur.wh[rt], sl, pr);
+    pr = mfma16(cur.wl[rt], sh, pr);
+    f32x4 po = mfma16(cur.qh[rt], sh, zero4());
+    po = mfma16(cur.qh[rt], sl, po);
+    red[buf][0][wave][rt][lane] = pr;
+    red[buf][1][wave][rt][lane] = po;
+  }
+  lds_barrier();
+  // Row tile `wave` of R = U - W S and of Q S (summed in wave order).
+  f32x4 r = cur.u, o = zero4();
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x4 a = red[buf][0][w][wave][lane], q = red[buf][1][w][wave][lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] -= a[e];
+      o[e] += q[e];
+    }
+  }
+  if (c == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] *= alpha;
+  }
+  {
+    bf16x8 t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bf16 hi, lo;
+      split_bf16(r[e], hi, lo);
+      t[e] = hi;
+      t[4 + e] = lo;
+    }
+    rb[buf][wave][lane] = t;
+  }
+  lds_barrier();
+  // R as 32-deep B operands over the chunk's tokens (k order pi32).
+  bf16x8 rh[2], rl[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 a = rb[buf][2 * ks][lane], z = rb[buf][2 * ks + 1][lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      rh[ks][e] = a[e];
+      rh[ks][4 + e] = z[e];
+      rl[ks][e] = a[4 + e];
+      rl[ks][4 + e] = z[4 + e];
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    o = mfma16(cur.mh[ks], rh[ks], o);
+    o = mfma16(cur.mh[ks], rl[ks], o);
+  }
+  {
+    const int tok0 = c * TC + 16 * wave + 4 * g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (tok0 + e < x.L)
+        x.o_inter[(((int64_t)x.b * x.L + tok0 + e) * x.H + x.h) * D + 16 * x.slice + r16] = o[e];
+  }
+  if (c == 0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[t][e] *= alpha;
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      st[t] = mfma16(cur.kh[t][ks], rh[ks], st[t]);
+      st[t] = mfma16(cur.kh[t][ks], rl[ks], st[t]);
+      st[t] = mfma16(cur.kl[t][ks], rh[ks], st[t]);
+    }
 }
 
 // Wavefront w keeps rows 32w .. 32w+31 (d_k) of the slice's 16 columns of S
 // as two accumulator tiles; it forms its share of W S and Q S, reduces row
 // tile w of R and O over the four shares, and updates its rows with K^T R.
-__global__ __launch_bounds__(256) void tl_recur_kernel(RecurParams p) {
-  __shared__ __attribute__((aligned(16))) f32x4 red[2][2][4][4][64];  // [buf][R/O][wave][tile][lane]
-  __shared__ __attribute__((aligned(16))) bf16x8 rb[2][4][64];        // [buf][tile][lane]: 4 hi, 4 lo
+// The operands of chunk c + 2 are loaded while chunk c runs (three register
+// sets in turn, so no set is copied and no load is waited for early).
+__global__ __launch_bounds__(256, 1) void tl_recur_kernel(RecurParams p) {
+  __shared__ __attribute__((aligned(16))) f32x4 red[2][2][4][4][64];
+  __shared__ __attribute__((aligned(16))) bf16x8 rb[2][4][64];
   const int bid = blockIdx.x;
   const int item = (bid & 7) * p.per_xcd + (bid >> 3);
   if (item >= p.nitems) return;
@@ -399,108 +502,28 @@ __global__ __launch_bounds__(256) void tl_recur_kernel(RecurParams p) {
   const int bh = item / NSL;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
-  const float alpha = p.alpha[bh];
   float *Sh = p.S + (int64_t)bh * D * D + 16 * slice + r16;
   f32x4 st[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) st[t][i] = Sh[(32 * wave + 16 * t + 4 * g + i) * D];
-  const int h = bh % p.H, b = bh / p.H;
+  const RecurCtx x{red, rb, p.o_inter, p.H, p.L, bh / p.H, bh % p.H, slice, wave, lane, g, r16,
+                   p.alpha[bh]};
   const char *rec0 = p.rec + (int64_t)bh * p.nchunk * REC;
-
-  ChunkOps cur, nxt;
-  load_ops(cur, rec0, wave, lane, slice);
-  for (int c = 0; c < p.nchunk; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < p.nchunk) load_ops(nxt, rec0 + (int64_t)(c + 1) * REC, wave, lane, slice);
-    // S rows of this wave as a 32-deep B operand (k order pi32).
-    float sv[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = st[0][e];
-      sv[4 + e] = st[1][e];
-    }
-    bf16x8 sh, sl;
-    split8(sv, sh, sl);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 pr = mfma16(cur.wh[rt], sh, zero4());
-      pr = mfma16(cur.wh[rt], sl, pr);
-      pr = mfma16(cur.wl[rt], sh, pr);
-      f32x4 po = mfma16(cur.qh[rt], sh, zero4());
-      po = mfma16(cur.qh[rt], sl, po);
-      red[buf][0][wave][rt][lane] = pr;
-      red[buf][1][wave][rt][lane] = po;
-    }
-    lds_barrier();
-    // Row tile `wave` of R = U - W S and of Q S (summed in wave order).
-    f32x4 r = cur.u, o = zero4();
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const f32x4 a = red[buf][0][w][wave][lane], q = red[buf][1][w][wave][lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r[e] -= a[e];
-        o[e] += q[e];
-      }
-    }
-    if (c == 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] *= alpha;
-    }
-    {
-      bf16x8 t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bf16 hi, lo;
-        split_bf16(r[e], hi, lo);
-        t[e] = hi;
-        t[4 + e] = lo;
-      }
-      rb[buf][wave][lane] = t;
-    }
-    lds_barrier();
-    // R as 32-deep B operands over the chunk's tokens (k order pi32).
-    bf16x8 rh[2], rl[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = rb[buf][2 * ks][lane], z = rb[buf][2 * ks + 1][lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        rh[ks][e] = a[e];
-        rh[ks][4 + e] = z[e];
-        rl[ks][e] = a[4 + e];
-        rl[ks][4 + e] = z[4 + e];
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      o = mfma16(cur.mh[ks], rh[ks], o);
-      o = mfma16(cur.mh[ks], rl[ks], o);
-    }
-    {
-      const int tok0 = c * TC + 16 * wave + 4 * g;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (tok0 + e < p.L)
-          p.o_inter[(((int64_t)b * p.L + tok0 + e) * p.H + h) * D + 16 * slice + r16] = o[e];
-    }
-    if (c == 0) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st[t][e] *= alpha;
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        st[t] = mfma16(cur.kh[t][ks], rh[ks], st[t]);
-        st[t] = mfma16(cur.kh[t][ks], rl[ks], st[t]);
-        st[t] = mfma16(cur.kl[t][ks], rh[ks], st[t]);
-      }
-    cur = nxt;
+  const int n = p.nchunk;
+  ChunkOps A, B, C;
+  load_ops(A, rec0, wave, lane, slice);
+  if (n > 1) load_ops(B, rec0 + REC, wave, lane, slice);
+  for (int c = 0; c < n; c += 3) {
+    if (c + 2 < n) load_ops(C, rec0 + (int64_t)(c + 2) * REC, wave, lane, slice);
+    recur_chunk(x, A, c, st);
+    if (c + 1 >= n) break;
+    if (c + 3 < n) load_ops(A, rec0 + (int64_t)(c + 3) * REC, wave, lane, slice);
+    recur_chunk(x, B, c + 1, st);
+    if (c + 2 >= n) break;
+    if (c + 4 < n) load_ops(B, rec0 + (int64_t)(c + 4) * REC, wave, lane, slice);
+    recur_chunk(x, C, c + 2, st);
   }
   if (p.update) {
 #pragma unroll
@@ -602,7 +625,7 @@ hipError_t launch_token_level_bf16(const TokenLevelArgs &a, hipStream_t s) {
     PrepParams pp{(const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                   (const bf16 *)a.Wq, (const bf16 *)a.Wk, (const bf16 *)a.Wv,
                   a.alpha, a.beta, a.H, a.L, nchunk, nitems, per_xcd, (char *)a.records};
-    hipLaunchKernelGGL(tl_prep_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, pp);
+    hipLaunchKernelGGL(tl_prep_kernel, dim3((unsigned)(8 * per_xcd)), dim3(512), 0, s, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -23,14 +23,16 @@
 // not depend on S, so:
 //   tl_prep_kernel  (one workgroup per stream, head and chunk, all in
 //                   parallel): projections, L2 norms, K K^T and Q K^T on the
-//                   matrix cores, W and U by forward substitution in fp32,
-//                   all stored as ready-made MFMA operands;
+//                   matrix cores, T by 16 x 16 blocks in fp32, W and U as
+//                   T times the right-hand sides on the matrix cores, all
+//                   stored as ready-made MFMA operands;
 //   tl_recur_kernel (one workgroup per stream, head and 16 state columns):
 //                   the chunks in order, S in registers.
 // Precision: products that feed the state (K K^T, W S, K^T R) use split
 // bf16 (x = hi + lo, three MFMAs; Henry, Tang and Heinecke, ARITH 2019);
 // the output-only products (Q K^T's use in O, Q S, M R) take Q and M in
-// plain bf16. The substitution runs in fp32.
+// plain bf16. T is formed in fp32; T times the right-hand sides uses split
+// bf16.
 #include "arl2_device.h"
 #include "arl2_kernels.h"
 
@@ -90,12 +92,13 @@ struct PrepParams {
 
 // Eight wavefronts. (A) waves 0-5 each project one 32-token tile of one map
 // (k, v, q); (B) waves 0-5 each form one 32x32 tile of K K^T or Q K^T while
-// waves 6-7 write the Q and K^T records; (C) waves 0-3 run the forward
-// substitution (one column per lane) while waves 4-7 write the M record;
-// (D) everyone writes the W and U records.
+// waves 6-7 write the Q and K^T records; (C) T = (I + A)^-1 by 16 x 16
+// blocks while waves 4-7 write the M record, then W and U = T x (right-hand
+// sides) on the matrix cores; (D) everyone writes the W and U records.
 __global__ __launch_bounds__(512) void tl_prep_kernel(PrepParams p) {
   __shared__ __attribute__((aligned(16))) float vecs[3][TC][VROW];  // Q', K', V' (then W, U)
   __shared__ __attribute__((aligned(16))) float gram[2][TC][GROW];  // beta-scaled K K^T, Q K^T
+  __shared__ __attribute__((aligned(16))) float tinv[TC][GROW];     // T = (I + A)^-1
   __shared__ float betas[TC], bgs[TC];
   const int bid = blockIdx.x;
   const int item = (bid & 7) * p.per_xcd + (bid >> 3);
@@ -106,6 +109,9 @@ __global__ __launch_bounds__(512) void tl_prep_kernel(PrepParams p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, r16 = lane & 15;
+  // T's strict upper part stays zero (its blocks on and below the diagonal
+  // are written in phase C).
+  for (int e = tid; e < TC * GROW; e += 512) (&tinv[0][0])[e] = 0.f;
   const int t0 = chunk * TC;
   const int nvalid = min(TC, p.L - t0);
   const int tokB = p.H * D * 2;
@@ -258,41 +264,31 @@ __global__ __launch_bounds__(512) void tl_prep_kernel(PrepParams p) {
   }
   __syncthreads();
 
-  // (C) waves 0-3: the forward substitution
-  //   (I + tril(diag(beta) K K^T, -1)) X = [diag(beta g) K | diag(beta) V],
-  // one column of X per lane; waves 4-7: the M = tril(Q K^T) record.
-  if (wave < 4) {
-    const bool isK = tid < D;
-    const int col = isK ? tid : tid - D;
-    float(*X)[VROW] = vecs[isK ? 1 : 2];
-    // Column order: once x_j is final, every later row takes its term
-    // (x_i -= beta_i (k'_i . k'_j) x_j). Each step is up to 63 independent
-    // FMAs on one broadcast LDS row; row j + 1 is read while row j's FMAs
-    // run (two row buffers).
-    float x[TC];
+  // (C) W = T diag(beta g) K and U = T diag(beta) V with
+  // T = (I + A)^-1, A = tril(diag(beta) K K^T, -1) (unit lower triangular),
+  // built from 16 x 16 blocks in fp32: the diagonal blocks by forward
+  // substitution, then the blocks below them one sub-diagonal at a time,
+  //   T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ,
+  // and finally X = T [diag(beta g) K | diag(beta) V] on the matrix cores
+  // (split bf16). Waves 4-7 write the M = tril(Q K^T) record meanwhile.
+  // A[i][j] is read as gram[0][j][i].
+  if (wave == 0) {
+    // Diagonal block I = lane / 16, column c = lane % 16, column order.
+    const int I = lane >> 4, c = lane & 15, o = 16 * I;
+    float t[16];
 #pragma unroll
-    for (int i = 0; i < TC; ++i) x[i] = X[i][col] * (isK ? bgs[i] : betas[i]);
-    f32x4 row[2][TC / 4];
+    for (int r = 0; r < 16; ++r) t[r] = r == c ? 1.f : 0.f;
 #pragma unroll
-    for (int i4 = 0; i4 < TC; i4 += 4) row[0][i4 / 4] = *(const f32x4 *)&gram[0][0][i4];
+    for (int j = 0; j < 15; ++j) {
+      float a[16];
 #pragma unroll
-    for (int j = 0; j < TC - 1; ++j) {
-      if (j + 1 < TC - 1) {
+      for (int r4 = 0; r4 < 16; r4 += 4) *(f32x4 *)&a[r4] = *(const f32x4 *)&gram[0][o + j][o + r4];
 #pragma unroll
-        for (int i4 = (j + 2) & ~3; i4 < TC; i4 += 4)
-          row[(j + 1) & 1][i4 / 4] = *(const f32x4 *)&gram[0][j + 1][i4];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i4 = (j + 1) & ~3; i4 < TC; i4 += 4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i4 + e > j) x[i4 + e] = fmaf(-row[j & 1][i4 / 4][e], x[j], x[i4 + e]);
-      }
+      for (int r = j + 1; r < 16; ++r) t[r] = fmaf(-a[r], t[j], t[r]);
     }
 #pragma unroll
-    for (int i = 0; i < TC; ++i) X[i][col] = x[i];
-  } else {
+    for (int r = 0; r < 16; ++r) tinv[o + r][o + c] = t[r];
+  } else if (wave >= 4) {
     const int rt = wave - 4, i = 16 * rt + r16;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -304,6 +300,76 @@ __global__ __launch_bounds__(512) void tl_prep_kernel(PrepParams p) {
       }
       *(bf16x8 *)(rec + OFF_M + (rt * 2 + ks) * 1024 + lane * 16) = mh;
     }
+  }
+  __syncthreads();
+  // Sub-diagonal d = 1, 2, 3: wave J < 4 - d forms block (J + d, J). Lane
+  // (r = l / 4, c4 = l % 4) owns row r, columns 4c4 .. 4c4+3 of the block.
+#pragma unroll
+  for (int dgl = 1; dgl < 4; ++dgl) {
+    if (wave < 4 - dgl) {
+      const int J = wave, I = J + dgl, r = lane >> 2, c4 = lane & 3;
+      // P = sum_{J <= K < I} A_IK T_KJ, row r.
+      f32x4 pr = {0.f, 0.f, 0.f, 0.f};
+      for (int K = J; K < I; ++K) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float a = gram[0][16 * K + k][16 * I + r];
+          const f32x4 tk = *(const f32x4 *)&tinv[16 * K + k][16 * J + 4 * c4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pr[e] = fmaf(a, tk[e], pr[e]);
+        }
+      }
+      // The block's own slot holds P until every lane has read what it needs.
+      *(f32x4 *)&tinv[16 * I + r][16 * J + 4 * c4] = pr;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+      f32x4 res = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float tik = tinv[16 * I + r][16 * I + k];
+        const f32x4 pk = *(const f32x4 *)&tinv[16 * I + k][16 * J + 4 * c4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[e] = fmaf(-tik, pk[e], res[e]);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+      *(f32x4 *)&tinv[16 * I + r][16 * J + 4 * c4] = res;
+    }
+    __syncthreads();
+  }
+  {
+    // X = T RHS: wave w takes columns 32w .. 32w+31 of [K | V] (K for
+    // w < 4), rows in two 32-row tiles, k in four steps of 16.
+    const int m = wave < 4 ? 1 : 2, col = 32 * (wave & 3) + l32;
+    float(*X)[VROW] = vecs[m];
+    const float *coef = wave < 4 ? bgs : betas;
+    f32x16 acc[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 16 * ks + 8 * hl;
+      float xb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[e] = X[k0 + e][col] * coef[k0 + e];
+      bf16x8 bh8, bl8;
+      split8(xb, bh8, bl8);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        float xa[8];
+        *(f32x4 *)&xa[0] = *(const f32x4 *)&tinv[32 * rt + l32][k0];
+        *(f32x4 *)&xa[4] = *(const f32x4 *)&tinv[32 * rt + l32][k0 + 4];
+        bf16x8 ah, al;
+        split8(xa, ah, al);
+        acc[rt] = mfma32(ah, bh8, acc[rt]);
+        acc[rt] = mfma32(ah, bl8, acc[rt]);
+        acc[rt] = mfma32(al, bh8, acc[rt]);
+      }
+    }
+    // Every read of this wave's columns is done (the values above fed the
+    // MFMAs); the results replace them.
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) X[32 * rt + 8 * (i >> 2) + 4 * hl + (i & 3)][col] = acc[rt][i];
   }
   __syncthreads();
 

@@ -36,6 +36,10 @@
  *    Two calls that share one state (its S or its workspace) must be
  *    ordered by the caller (same stream, or events).
  *  - Results are bitwise reproducible run to run: no floating-point atomics.
+ *  - The compute entry points only launch kernels on `stream` (no memsets,
+ *    no host synchronisation, no allocation), so a caller may capture them
+ *    into a HIP graph and replay it; a replay gives the bytes the same calls
+ *    give eagerly. Kernel timing (arl2_profile_enable) is the exception.
  */
 #ifndef ARL2_H
 #define ARL2_H

@@ -380,6 +380,9 @@ def main() -> int:
     ap.add_argument("--gate-projections-only", action="store_true",
                     help="only time the gate projections on the workload's shape and print "
                          "their JSON object")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the cycle of distinct frames into one HIP graph and time its "
+                         "replays instead of eager calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB 10 times (scales the HBM byte "
@@ -445,26 +448,45 @@ def main() -> int:
     out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step(i, s=stream):
         for p in frames[i % len(frames)]:
             if args.access == "token":
-                layer.forward_token_level(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update,
-                                          stream)
+                layer.forward_token_level(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, s)
             else:
-                layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, stream,
+                layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, s,
                               gate=w.gate)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph:
+        # The cycle of distinct frames as one HIP graph, replayed steps / cycle times.
+        if args.steps % len(frames):
+            print(f"bench.py: --graph needs --steps to be a multiple of {len(frames)}",
+                  file=sys.stderr)
+            return 2
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for i in range(len(frames)):
+                step(i, cap)
+        torch.cuda.synchronize()
+        graph.replay()          # one untimed replay
+        torch.cuda.synchronize()
+
     # ---- timed region (single process: the barrier is the synchronize)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    if graph is not None:
+        for _ in range(args.steps // len(frames)):
+            graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -504,6 +526,7 @@ def main() -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "d": d, "L": L,
+                   "launch": "HIP graph replay" if graph is not None else "eager",
                    "passes_per_frame": f"{w.noisy_passes} query-only + 1 clean",
                    "distinct_frames_cycled": NUM_DISTINCT_FRAMES},
         "tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -65,6 +65,10 @@ struct CombineKParams {
 // m_s. Lanes own queries and registers own d_v, as in the attention
 // kernel's accumulators, so the partials are read in the order they were
 // written and O_inter comes out of the MFMAs in the same layout.
+// Every load is issued before any arithmetic: the state rows (converted to
+// bf16 into LDS first, which frees their registers), W_q, the queries, the
+// merge weights and the first kPre key ranges' partials. The merge runs
+// first and the inter-frame read's last product accumulates onto it.
 // Wt: 32 KB of LDS for W_q[h], then the output rows; St: 32 KB for bf16(S).
 __device__ __forceinline__ void combine_body(const CombineKParams p, int item, char *Wt,
                                              char *St) {
@@ -77,9 +81,39 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
   const int qrow = qblk * kQBlock + wave * 32 + l32;
   const bool inter = p.Wq != nullptr;
 
-  // Loads that do not depend on the inter-frame read go first: the merge
-  // weights of the key ranges for this lane's query and the first range's
-  // partial (16-byte units in the order the attention kernel wrote them).
+  // State rows (fp32) and W_q[h] (straight into LDS, swizzled).
+  f32x4 sx[8][2];
+  bf16x8 qop[8];
+  if (inter) {
+    const float *Sh = p.S + ((int64_t)b * p.H + h) * D * D;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = (tid >> 4) + 16 * i, u = tid & 15;
+      sx[i][0] = *(const f32x4 *)(Sh + row * D + 8 * u);
+      sx[i][1] = *(const f32x4 *)(Sh + row * D + 8 * u + 4);
+    }
+    const bf16 *W = p.Wq + (int64_t)h * D * D;
+    const int r4 = lane >> 4, pos = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int cc = 8 * wave + i, row = 4 * cc + r4;
+      global_to_lds16(W + row * D + 8 * (pos ^ tile_swz(row & 15)), Wt + cc * 1024);
+    }
+    // The wave's 32 queries as B operands: lane l holds query l%32,
+    // features 16c + 8*(l/32) .. +7 (zeros past the frame).
+    if (qrow < p.L) {
+      const bf16 *qp = p.q + ((int64_t)b * p.L + qrow) * tok + (int64_t)h * D + 8 * hl;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) qop[c] = *(const bf16x8 *)(qp + 16 * c);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) qop[c] = zero_bf16x8();
+    }
+  }
+
+  // Merge weights of the key ranges for this lane's query, and the first
+  // kPre ranges' partials (16-byte units in the order the attention kernel
+  // wrote them); further ranges stream through the same registers.
   const int64_t blk0 = (int64_t)item * p.nsplit;
   const int qi = wave * 32 + l32;
   float mv[kMaxSplit], lv[kMaxSplit];
@@ -91,45 +125,66 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
       lv[s] = ml[1];
     }
   const char *src = p.ws_o + blk0 * kPartialOBytes + (wave * 8 * 64 + lane) * 16;
-  bf16x8 cur[8], nxt[8];
+  constexpr int kPre = 3;
+  bf16x8 pr[kPre][8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) cur[u] = *(const bf16x8 *)(src + u * 64 * 16);
-
-  f32x16 acc[4];
-  if (inter) {
-    // W_q[h] (copied straight into LDS, swizzled) and bf16(S[b][h]).
-    const bf16 *W = p.Wq + (int64_t)h * D * D;
-    const int r4 = lane >> 4, pos = lane & 15;
+  for (int s = 0; s < kPre; ++s)
+    if (s < p.nsplit) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int cc = 8 * wave + i, row = 4 * cc + r4;
-      global_to_lds16(W + row * D + 8 * (pos ^ tile_swz(row & 15)), Wt + cc * 1024);
+      for (int u = 0; u < 8; ++u)
+        pr[s][u] = *(const bf16x8 *)(src + s * kPartialOBytes + u * 64 * 16);
     }
-    const float *Sh = p.S + ((int64_t)b * p.H + h) * D * D;
+
+  if (inter) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = (tid >> 4) + 16 * i, u = tid & 15;
-      const f32x4 x0 = *(const f32x4 *)(Sh + row * D + 8 * u);
-      const f32x4 x1 = *(const f32x4 *)(Sh + row * D + 8 * u + 4);
       bf16x8 t;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        t[e] = (bf16)x0[e];
-        t[4 + e] = (bf16)x1[e];
+        t[e] = (bf16)sx[i][0][e];
+        t[4 + e] = (bf16)sx[i][1][e];
       }
       *(bf16x8 *)(St + tile_off(row, u)) = t;
     }
-    // The wave's 32 queries as B operands: lane l holds query l%32,
-    // features 16c + 8*(l/32) .. +7 (zeros past the frame).
-    bf16x8 qop[8];
-    if (qrow < p.L) {
-      const bf16 *qp = p.q + ((int64_t)b * p.L + qrow) * tok + (int64_t)h * D + 8 * hl;
+  }
+
+  float M = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) qop[c] = *(const bf16x8 *)(qp + 16 * c);
-    } else {
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < p.nsplit) M = fmaxf(M, mv[s]);
+  float Lt = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) qop[c] = zero_bf16x8();
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < p.nsplit) {
+      lv[s] *= exp2_fast(mv[s] - M);
+      Lt += lv[s];
     }
+  const float il = 1.f / Lt;
+  // acc = sum_s (w_s / sum w) Ohat_s, range by range in range order.
+  f32x16 acc[4];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) acc[bb] = zero16();
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < p.nsplit) {
+      const float w = lv[s] * il;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[bb][8 * r2 + e] =
+                fmaf(w, (float)pr[s % kPre][2 * bb + r2][e], acc[bb][8 * r2 + e]);
+      if (s + kPre < p.nsplit) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          pr[s % kPre][u] = *(const bf16x8 *)(src + (s + kPre) * kPartialOBytes + u * 64 * 16);
+      }
+    }
+
+  if (inter) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -154,11 +209,10 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
       for (int i = 0; i < 16; ++i) ss = fmaf(qp4[bb][i], qp4[bb][i], ss);
     ss += swap_halves(ss);
     const float inv = 1.f / fmaxf(sqrtf(ss), kL2Eps);
-    // O_inter^T = S^T Q'^T with Q' fed from the accumulators: register
-    // 8*(g%2) + j of block g/2 holds feature 16g + swap_bits23(8*(l/32) + j),
-    // i.e. rows 16g + 4*(l/32) + {0..3} and 16g + 8 + 4*(l/32) + {0..3} of S.
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) acc[bb] = zero16();
+    // acc += O_inter^T = S^T Q'^T with Q' fed from the accumulators:
+    // register 8*(g%2) + j of block g/2 holds feature 16g +
+    // swap_bits23(8*(l/32) + j), i.e. rows 16g + 4*(l/32) + {0..3} and
+    // 16g + 8 + 4*(l/32) + {0..3} of S.
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       bf16x8 qb;
@@ -181,46 +235,9 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
       for (int r = 0; r < 4; ++r) {
         const f32x4 x = qrow < p.L ? *(const f32x4 *)(oi + 32 * bb + 8 * r) : zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[bb][4 * r + e] = x[e];
+        for (int e = 0; e < 4; ++e) acc[bb][4 * r + e] += x[e];
       }
-  } else {
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) acc[bb] = zero16();
   }
-
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s)
-    if (s < p.nsplit) M = fmaxf(M, mv[s]);
-  float Lt = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s)
-    if (s < p.nsplit) {
-      lv[s] *= exp2_fast(mv[s] - M);
-      Lt += lv[s];
-    }
-  const float il = 1.f / Lt;
-  // acc += (w_s / sum w) Ohat_s, range by range, the next range's 16-byte
-  // units in flight while the current one is added.
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s)
-    if (s < p.nsplit) {
-      if (s + 1 < p.nsplit) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          nxt[u] = *(const bf16x8 *)(src + (s + 1) * kPartialOBytes + u * 64 * 16);
-      }
-      const float w = lv[s] * il;
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            acc[bb][8 * r2 + e] = fmaf(w, (float)cur[2 * bb + r2][e], acc[bb][8 * r2 + e]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
-    }
 
   // Output rows through LDS: the wave's 32 rows as a swizzled 32 x 256-byte
   // tile in Wt (free once every wave is past the inter-frame read), then

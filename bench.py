@@ -20,6 +20,10 @@ Prints one JSON line (the driver's contract) with, besides frames/s:
                 with HIP events on its launch stream (arl2_profile_*) in a
                 leg after the timed region, each idempotent kernel launched
                 --profile-repeat times back to back per event pair;
+  mfma_loop_peak_tflops  the bf16 MFMA rate a pure matrix-core loop sustains
+                on this device in the same run (arl2_profile_mfma_peak), the
+                measured counterpart of the published peak; roofline.frac
+                stays against the published peak;
   cpu_baseline  the float64 oracle on this host's cores, on a bounded sample.
 """
 from __future__ import annotations
@@ -505,6 +509,7 @@ def main() -> int:
     kern_us = {k: 1000.0 * ms / n for k, (n, ms) in rep.items() if n}
 
     gate_leg = gate_projection_leg(w, dev, stream, 20, 50)
+    mfma_loop = max(Bd.arl2_profile_mfma_peak(4096, stream) for _ in range(3))
 
     fa, fb, fc = flops(B, H, d, L)
     passes = w.passes_per_frame
@@ -518,7 +523,8 @@ def main() -> int:
                 "traffic": measured_traffic("attn_partial", args.workload, digest),
                 "kernel": "attn_partial",
                 "per_launch": f"4*B*H*L^2*d = {fa / 1e9:.3f} GFLOP (one pass, B={B} H={H} L={L} d={d})",
-                "avg_launch_us": round(kern_us["attn_partial"], 2)}
+                "avg_launch_us": round(kern_us["attn_partial"], 2),
+                "frac_of_measured_mfma_loop": round(att_tflops / mfma_loop, 4)}
 
     res = {
         "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1,
@@ -534,6 +540,7 @@ def main() -> int:
         "event_ms_per_step": round(ev_ms / args.steps, 5),
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": roofline,
+        "mfma_loop_peak_tflops": round(mfma_loop, 1),
         "gate_projections": gate_leg,
     }
     if not args.no_cpu_baseline:

@@ -80,6 +80,7 @@ def _load() -> ctypes.CDLL:
         "arl2_profile_enable": (I, [I, I]),
         "arl2_profile_report": (I, [ctypes.c_char_p, Z]),
         "arl2_profile_reset": (None, []),
+        "arl2_profile_mfma_peak": (I, [I, ctypes.POINTER(ctypes.c_double), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -95,7 +96,8 @@ EXPORTED = ("arl2_version", "arl2_status_string", "arl2_last_error", "arl2_works
             "arl2_softmax_attention_workspace_bytes", "arl2_softmax_attention",
             "arl2_gate_projections_workspace_bytes", "arl2_gate_projections",
             "arl2_token_level_workspace_bytes", "arl2_frame_forward_token_level",
-            "arl2_profile_enable", "arl2_profile_report", "arl2_profile_reset")
+            "arl2_profile_enable", "arl2_profile_report", "arl2_profile_reset",
+            "arl2_profile_mfma_peak")
 
 
 def _ptr(x):
@@ -204,6 +206,13 @@ def arl2_profile_enable(on: bool, repeat: int = 1) -> None:
 
 def arl2_profile_reset() -> None:
     _lib.arl2_profile_reset()
+
+
+def arl2_profile_mfma_peak(iters: int = 4096, stream=None) -> float:
+    """Sustained bf16 MFMA rate of the current device in TFLOP/s (a pure MFMA loop)."""
+    out = ctypes.c_double(0.0)
+    _check(_lib.arl2_profile_mfma_peak(int(iters), ctypes.byref(out), _stream(stream)))
+    return out.value
 
 
 def arl2_profile_report() -> dict:

@@ -698,4 +698,35 @@ arl2_status arl2_profile_report(char *buf, size_t len) {
   return ok();
 }
 
+arl2_status arl2_profile_mfma_peak(int32_t iters, double *tflops, void *stream) {
+  static const char *fn = "arl2_profile_mfma_peak";
+  if (!tflops) return fail(ARL2_ERR_INVALID_ARG, "%s: tflops is NULL", fn);
+  if (iters < 1 || iters > (1 << 20))
+    return fail(ARL2_ERR_INVALID_ARG, "%s: iters %d not in [1, 2^20]", fn, iters);
+  hipStream_t s = (hipStream_t)stream;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (cus < 1) return fail(ARL2_ERR_HIP, "%s: no compute units reported", fn);
+  float *sink = nullptr;
+  hipEvent_t t0 = nullptr, t1 = nullptr;
+  if ((e = hipMalloc((void **)&sink, (size_t)cus * 512 * sizeof(float))) != hipSuccess)
+    return hip_status(e, fn);
+  float ms = 0.f;
+  if ((e = hipEventCreate(&t0)) == hipSuccess && (e = hipEventCreate(&t1)) == hipSuccess &&
+      (e = arl2::launch_mfma_peak(cus, 16, sink, s)) == hipSuccess &&  // warm-up
+      (e = hipEventRecord(t0, s)) == hipSuccess &&
+      (e = arl2::launch_mfma_peak(cus, iters, sink, s)) == hipSuccess &&
+      (e = hipEventRecord(t1, s)) == hipSuccess && (e = hipEventSynchronize(t1)) == hipSuccess)
+    e = hipEventElapsedTime(&ms, t0, t1);
+  if (t0) (void)hipEventDestroy(t0);
+  if (t1) (void)hipEventDestroy(t1);
+  (void)hipFree(sink);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (!(ms > 0.f)) return fail(ARL2_ERR_HIP, "%s: the events measured no time", fn);
+  *tflops = arl2::mfma_peak_flops(cus, iters) / ((double)ms * 1e-3) / 1e12;
+  return ok();
+}
+
 }  // extern "C"

@@ -138,4 +138,9 @@ hipError_t launch_generic_delta_partial(int dtype, int d, const void *k, const v
                                         const float *beta, int B, int H, int L, float *ws_dS,
                                         hipStream_t s);
 
+// Pure bf16 MFMA loop (one 512-thread workgroup per block; `sink` holds
+// blocks x 512 floats) and the flops one launch performs.
+hipError_t launch_mfma_peak(int blocks, int iters, float *sink, hipStream_t s);
+double mfma_peak_flops(int blocks, int iters);
+
 }  // namespace arl2

@@ -266,6 +266,24 @@ ARL2_API arl2_status arl2_profile_enable(int32_t on, int32_t repeat);
 ARL2_API arl2_status arl2_profile_report(char *buf, size_t len);
 ARL2_API void arl2_profile_reset(void);
 
+/*
+ * Measure the bf16 matrix-core rate the current device sustains: one
+ * launch of a pure MFMA loop (no memory traffic) with one 512-thread
+ * workgroup per compute unit, each wavefront running `iters` rounds of four
+ * independent 32x32x16 bf16 MFMA chains, timed with a pair of HIP events on
+ * `stream` after one short warm-up launch. *tflops receives the flops
+ * performed divided by the measured time, in TFLOP/s. It is the measured
+ * counterpart of the published dense bf16 peak, against which a kernel's
+ * fraction of peak is read. The call allocates and frees a small device
+ * buffer and waits for the stream: not for use under graph capture.
+ *   iters   rounds per wavefront, in [1, 2^20] (4096 gives about 0.5 ms on
+ *           MI355X).
+ *   tflops  host pointer, written on success only.
+ * Errors: INVALID_ARG for a NULL tflops or iters out of range; ARL2_ERR_HIP
+ * if the device query, the allocation, a launch or the events fail.
+ */
+ARL2_API arl2_status arl2_profile_mfma_peak(int32_t iters, double *tflops, void *stream);
+
 /* Static text for a status code (never NULL). */
 ARL2_API const char *arl2_status_string(int32_t status);
 

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert {"arl2_state_init", "arl2_state_reset", "arl2_frame_forward",
             "arl2_frame_forward_gated", "arl2_workspace_bytes"} <= names
-    assert len(names) == 17
+    assert len(names) == 18
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -53,6 +53,14 @@ def test_profile_report_without_launches(B):
         with pytest.raises(B.ARL2Error, match="repeat"):
             B.arl2_profile_enable(True, bad)
     B.arl2_profile_enable(False, 1)
+
+
+def test_mfma_peak_rejects_bad_arguments_before_touching_the_device(B):
+    for bad in (0, -5, (1 << 20) + 1):
+        with pytest.raises(B.ARL2Error, match="iters"):
+            B.arl2_profile_mfma_peak(bad)
+    assert B._lib.arl2_profile_mfma_peak(16, None, None) == B.ARL2_ERR_INVALID_ARG
+    assert "tflops" in B.arl2_last_error()
 
 
 def test_version_and_status_strings(B):

@@ -24,7 +24,9 @@ Prints one JSON line (the driver's contract) with, besides frames/s:
                 on this device in the same run (arl2_profile_mfma_peak), the
                 measured counterpart of the published peak; roofline.frac
                 stays against the published peak;
-  cpu_baseline  the float64 oracle on this host's cores, on a bounded sample.
+  cpu_baseline  the float64 oracle on this host's cores, on a bounded sample
+                (frames/s, and GFLOP/s on the same flop count as the GPU figure;
+                cores = the BLAS threads it used).
 """
 from __future__ import annotations
 
@@ -104,7 +106,11 @@ def cpu_baseline(frames_host, W, w, budget_s=15.0, max_frames=400, access="frame
     scale = w.B * w.H if one_head else 1
     what = (f"one (stream, head) of {done} frames, scaled by {scale}" if one_head
             else f"{done} full frames, all {w.B * w.H} (stream, head) pairs")
-    return {"value": done / dt / scale, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+    fa, fb, fc = flops(w.B, w.H, w.d, w.L)
+    fps = done / dt / scale
+    return {"value": fps, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "gflops": round(fps * (w.passes_per_frame * (fa + fb) + fc) / 1e9, 2),
+            "host_cpu_count": os.cpu_count(),
             "sample": f"{what} ({w.noisy_passes} query-only + 1 clean pass each) of {w.name}, "
                       f"float64 NumPy/OpenBLAS, {dt:.1f} s"}
 

@@ -76,6 +76,30 @@ def measured_traffic(kernel, workload, digest):
     return t.get("bytes_per_launch")
 
 
+def epilogue_bytes(B, H, d, L):
+    """Bytes each memory-bound launch of a pass must move (each input read
+    once, each output written once), for the bf16 d = 128 path: the combine
+    reads the key-range partials (bf16 O/l plus fp32 max and sum per query),
+    q, S and W_q and writes out; the delta chunks read k, v, W_k, W_v, S and
+    beta and write one fp32 d x d contribution per chunk of 128 tokens;
+    delta_apply reads those and S and writes S. The key-range count follows
+    the attention plan (two workgroups per CU, at least two 64-key tiles per
+    range, at most 8 ranges)."""
+    nqblk = -(-L // 128)
+    base = B * H * nqblk
+    ns = max(1, min(512 // base, -(-L // 128), 8))
+    kps = -(-(-(-L // ns)) // 64) * 64
+    nsplit = -(-L // kps)
+    io = B * L * H * d * 2
+    state = B * H * d * d * 4
+    partials = B * H * nqblk * nsplit * (128 * d * 2 + 128 * 2 * 4)
+    nchunk = -(-L // 128)
+    ds = B * H * nchunk * d * d * 4
+    combine = partials + io + state + H * d * d * 2 + io
+    delta = 2 * io + 2 * H * d * d * 2 + state + B * L * H * 4 + ds
+    return {"combine": combine, "combine_delta": combine + delta, "delta_apply": ds + 2 * state}
+
+
 def cpu_baseline(frames_host, W, w, budget_s=15.0, max_frames=400, access="frame"):
     """Time the float64 oracle on host copies of the same frames. Workloads
     whose full frame would not fit the budget are timed on one (stream,
@@ -516,6 +540,14 @@ def main() -> int:
 
     gate_leg = gate_projection_leg(w, dev, stream, 20, 50)
     mfma_loop = max(Bd.arl2_profile_mfma_peak(4096, stream) for _ in range(3))
+    epilogues = {}
+    if d == 128 and w.dtype == SI.BF16 and args.access == "frame":
+        for name, nbytes in epilogue_bytes(B, H, d, L).items():
+            if name in kern_us:
+                gbs = nbytes / (kern_us[name] * 1e-6) / 1e9
+                epilogues[name] = {"bound": "hbm", "bytes": int(nbytes), "avg_launch_us": round(kern_us[name], 2),
+                                   "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
     fa, fb, fc = flops(B, H, d, L)
     passes = w.passes_per_frame
@@ -547,6 +579,7 @@ def main() -> int:
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": roofline,
         "mfma_loop_peak_tflops": round(mfma_loop, 1),
+        "epilogues": epilogues,
         "gate_projections": gate_leg,
     }
     if not args.no_cpu_baseline:

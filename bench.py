@@ -76,26 +76,32 @@ def measured_traffic(kernel, workload, digest):
     return t.get("bytes_per_launch")
 
 
-def epilogue_bytes(B, H, d, L):
-    """Bytes each memory-bound launch of a pass must move (each input read
-    once, each output written once), for the bf16 d = 128 path: the combine
-    reads the key-range partials (bf16 O/l plus fp32 max and sum per query),
-    q, S and W_q and writes out; the delta chunks read k, v, W_k, W_v, S and
-    beta and write one fp32 d x d contribution per chunk of 128 tokens;
-    delta_apply reads those and S and writes S. The key-range count follows
-    the attention plan (two workgroups per CU, at least two 64-key tiles per
-    range, at most 8 ranges)."""
+def workspace_parts(B, H, d, L):
+    """Bytes of the key-range partials (bf16 O/l, then fp32 max and sum per
+    query) and of the delta chunks' fp32 d x d contributions that one pass of
+    the bf16 d = 128 path keeps between its launches. The key-range count
+    follows the attention plan (two workgroups per CU, at least two 64-key
+    tiles per range, at most 8 ranges); the chunks hold 128 tokens."""
     nqblk = -(-L // 128)
     base = B * H * nqblk
     ns = max(1, min(512 // base, -(-L // 128), 8))
     kps = -(-(-(-L // ns)) // 64) * 64
     nsplit = -(-L // kps)
+    blocks = B * H * nqblk * nsplit
+    nchunk = -(-L // 128)
+    return blocks * 128 * d * 2, blocks * 128 * 2 * 4, B * H * nchunk * d * d * 4
+
+
+def epilogue_bytes(B, H, d, L):
+    """Bytes each memory-bound launch of a pass must move (each input read
+    once, each output written once) on the bf16 d = 128 path: the combine
+    reads the key-range partials, q, S and W_q and writes out; the delta
+    chunks read k, v, W_k, W_v, S and beta and write their contributions;
+    delta_apply reads those and S and writes S."""
+    o_bytes, ml_bytes, ds = workspace_parts(B, H, d, L)
     io = B * L * H * d * 2
     state = B * H * d * d * 4
-    partials = B * H * nqblk * nsplit * (128 * d * 2 + 128 * 2 * 4)
-    nchunk = -(-L // 128)
-    ds = B * H * nchunk * d * d * 4
-    combine = partials + io + state + H * d * d * 2 + io
+    combine = o_bytes + ml_bytes + io + state + H * d * d * 2 + io
     delta = 2 * io + 2 * H * d * d * 2 + state + B * L * H * 4 + ds
     return {"combine": combine, "combine_delta": combine + delta, "delta_apply": ds + 2 * state}
 

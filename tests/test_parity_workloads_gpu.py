@@ -169,6 +169,20 @@ def test_long231_480p_literal(lay, torch):
     _check(recs, out_errs, w.name, before_frame=min(first_ref, first_gpu))
 
 
+def test_maximum_frame_length(lay, torch):
+    """The longest frame the library accepts (ARL2_MAX_L = 2^20 tokens, one
+    head): one query-only and one clean pass. The attention then runs every
+    query block over all 16,384 key tiles in one key range, and the state
+    update sums 8,192 chunk contributions; the whole state and sampled output
+    rows are compared with the oracle."""
+    w = SI.Workload("max_frame_length", 1, 1, 128, 1 << 20, 1, 1, SI.BF16, 0.02, seed=2020)
+    t0 = time.time()
+    recs, out_errs, _ = _stream(lay, torch, w, rows_n=8)
+    print(f"maximum frame length took {time.time() - t0:.1f} s")
+    assert len(recs) == 1 and recs[0]["gpu_finite"] and recs[0]["ref_finite"]
+    _check(recs, out_errs, w.name)
+
+
 def test_batched720p(lay, torch):
     """Four independent streams (seeds 0..3) at the 720p latent shape
     (L = 3600), 21 frames of 4 query-only + 1 clean pass; sampled outputs

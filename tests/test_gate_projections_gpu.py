@@ -62,6 +62,7 @@ def _run(lay, B, L, D, H, dtype, seed):
     (1, 130, 100, 5, SI.BF16),      # D not a multiple of 64: generic kernel
     (2, 50, 48, 3, SI.F32),         # fp32 io
     (1, 3600, 1536, 12, SI.BF16),   # 720p frame: 45x80 tokens
+    (1, 37, 1 << 16, 3, SI.BF16),   # the widest input accepted (D = 2^16)
 ])
 def test_gate_projections_match_oracle(lay, B, L, D, H, dtype):
     ga, gb, a_ref, b_ref, tol_a, tol_b = _run(lay, B, L, D, H, dtype, seed=B * 1000 + L)

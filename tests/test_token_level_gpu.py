@@ -72,6 +72,50 @@ def test_token_level_mfma_path(lay, B, H, L, frames, noisy):
     assert kept
 
 
+@pytest.mark.parametrize("Bn,H", [(1, 65535), (65535, 1)])
+def test_token_level_maximum_heads_and_streams(lay, Bn, H):
+    """Token-level access with the largest head and stream counts accepted
+    (65,535), 64-token frames (one chunk record per (stream, head)): one
+    noisy and one clean pass drawn on the GPU; the first, last and middle
+    (stream, head) pairs are checked against the oracle."""
+    import torch
+    L, d = 64, 128
+    dev = device()
+    g = torch.Generator(device=dev)
+    g.manual_seed(Bn * 11 + H)
+    W = (torch.eye(d, device=dev) + 0.01 * torch.randn((3, H, d, d), generator=g, device=dev))
+    W = W.to(torch.bfloat16)
+    S0 = 0.02 * torch.randn((Bn, H, d, d), generator=g, device=dev)
+    layer = lay.ARL2Layer(Bn, H, d, L, 0)
+    layer.reset(S0)
+    out = torch.empty((Bn, L, H, d), dtype=torch.bfloat16, device=dev)
+    pairs = sorted({(0, 0), (Bn - 1, H - 1), (Bn // 2, H // 2), (Bn - 1, 0), (0, H - 1)})
+    S_ref = {bh: S0[bh].double().cpu().numpy() for bh in pairs}
+    for update in (0, 1):
+        q, k, v = (torch.randn((Bn, L, H, d), generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(3))
+        alpha = torch.sigmoid(2 + 0.5 * torch.randn((Bn, H), generator=g, device=dev))
+        beta = torch.sigmoid(torch.randn((Bn, L, H), generator=g, device=dev))
+        layer.forward_token_level(q, k, v, W, alpha, beta, out, update)
+        torch.cuda.synchronize()
+        for b, h in pairs:
+            def one(t):
+                return t[b:b + 1, :, h:h + 1].float().cpu().numpy()
+            Sh = S_ref[(b, h)][None, None].copy()
+            ref = O.token_level_frame_forward(one(q), one(k), one(v),
+                                              W[:, h:h + 1].float().cpu().numpy(), Sh,
+                                              alpha[b:b + 1, h:h + 1].cpu().numpy(),
+                                              beta[b:b + 1, :, h:h + 1].cpu().numpy(), update)
+            err = np.max(np.abs(one(out) - ref)) / np.max(np.abs(ref))
+            assert err <= TOL_OUT[SI.BF16], (b, h, update, err)
+            if update:
+                S_ref[(b, h)] = Sh[0, 0]
+    for b, h in pairs:
+        ref = S_ref[(b, h)]
+        err = np.max(np.abs(layer.S[b, h].double().cpu().numpy() - ref)) / np.max(np.abs(ref))
+        assert err <= TOL_S, (b, h, err)
+
+
 def test_token_level_480p_frame(lay):
     """The 480p frame step (12 heads, 1560 tokens = 24 chunks + 24 tokens):
     one noisy and one clean pass from a warm state."""

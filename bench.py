@@ -428,6 +428,7 @@ def main() -> int:
                     help="only copy a buffer of this many MiB 10 times (scales the HBM byte "
                          "counters of a profiler run) and exit")
     args = ap.parse_args()
+
     if args.calibrate_copy_mib:
         import torch
         n = args.calibrate_copy_mib << 20
@@ -439,8 +440,8 @@ def main() -> int:
         print(json.dumps({"copied_bytes_per_launch": n, "launches": 10}))
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(heads and streams shard with no exchange; see the sharding note in the design)",
+        print(f"bench.py: the benchmark measures one GPU; --gpus {args.gpus} is not supported "
+              "(the layer would shard by stream and head, with no exchange between GPUs)",
               file=sys.stderr)
         return 2
     if args.per_frame_report:

@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -270,3 +271,13 @@ def test_binding_refuses_to_load_without_the_library(repo_root):
     ])
     r = subprocess.run(["python", "-c", code], capture_output=True, text=True)
     assert "raised" in r.stdout, r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu(repo_root):
+    """The benchmark measures one GPU; asking for more exits with status 2
+    and says so, before touching any device."""
+    r = subprocess.run([sys.executable, os.path.join(repo_root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 2 is not supported" in r.stderr
+    assert r.stdout == ""

@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
   ARL2_OK = 0,
   ARL2_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, bad size or flag     */
-  ARL2_ERR_UNSUPPORTED = 2, /* a valid request this build does not handle    */
+  ARL2_ERR_UNSUPPORTED = 2, /* a valid request the library does not handle   */
   ARL2_ERR_HIP = 3          /* the HIP runtime refused a launch or a copy    */
 } arl2_status;
 
@@ -71,7 +71,7 @@ typedef enum {
   ARL2_F32 = 1   /* q, k, v, W_phi, out stored as float32  */
 } arl2_dtype;
 
-/* Head dimensions this build supports (d_k = d_v = d). */
+/* Head dimensions the library supports (d_k = d_v = d). */
 #define ARL2_D_SMALL 16
 #define ARL2_D_LARGE 128
 

@@ -81,14 +81,16 @@ def workspace_parts(B, H, d, L):
     query) and of the delta chunks' fp32 d x d contributions that one pass of
     the bf16 d = 128 path keeps between its launches. The key-range count
     follows the attention plan (two workgroups per CU, at least two 64-key
-    tiles per range, at most 8 ranges); the chunks hold 128 tokens."""
+    tiles per range, at most 8 ranges); the chunks hold 96 tokens when the
+    delta chunks and the combine's query blocks fit 512 workgroups, else 128."""
     nqblk = -(-L // 128)
     base = B * H * nqblk
     ns = max(1, min(512 // base, -(-L // 128), 8))
     kps = -(-(-(-L // ns)) // 64) * 64
     nsplit = -(-L // kps)
     blocks = B * H * nqblk * nsplit
-    nchunk = -(-L // 128)
+    chunk = 96 if B * H * (-(-L // 96) + nqblk) <= 512 else 128
+    nchunk = -(-L // chunk)
     return blocks * 128 * d * 2, blocks * 128 * 2 * 4, B * H * nchunk * d * d * 4
 
 

@@ -81,7 +81,7 @@ arl2_status check_shape(int64_t B, int64_t H, int64_t d, int64_t L, int64_t dtyp
 struct FramePlan {
   bool mfma = false;
   arl2::AttnPlan ap;
-  int nchunk = 0;
+  int chunk = 0, nchunk = 0;  // tokens per delta chunk, chunks per frame
   size_t off_o = 0, off_ml = 0, off_ds = 0, total = 0;
 };
 
@@ -94,10 +94,12 @@ FramePlan plan_frame(int64_t B, int64_t H, int64_t d, int64_t L, int32_t dtype) 
     const size_t blocks = (size_t)B * H * fp.ap.nqblk * fp.ap.nsplit;
     o_bytes = blocks * arl2::kPartialOBytes;
     ml_bytes = blocks * arl2::kPartialML * sizeof(float);
-    fp.nchunk = (int)((L + arl2::kDeltaChunk - 1) / arl2::kDeltaChunk);
+    fp.chunk = arl2::delta_chunk_tokens(B, H, L);
+    fp.nchunk = (int)((L + fp.chunk - 1) / fp.chunk);
   } else {
     o_bytes = (size_t)B * H * L * d * sizeof(float);
     ml_bytes = 0;
+    fp.chunk = arl2::kGenChunk;
     fp.nchunk = (int)((L + arl2::kGenChunk - 1) / arl2::kGenChunk);
   }
   const size_t ds_bytes = (size_t)B * H * fp.nchunk * d * d * sizeof(float);
@@ -371,7 +373,7 @@ arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, con
   if (fp.mfma) {
     const arl2::AttnArgs aa{q, k, v, iB, iH, iL, iL, fp.ap, ws_o, ws_ml};
     const arl2::CombineArgs ca{ws_o, ws_ml, q, Wq, S, iB, iH, iL, fp.ap, out};
-    const arl2::DeltaArgs da{k, v, Wk, Wv, S, beta, iB, iH, iL, fp.nchunk, ws_ds};
+    const arl2::DeltaArgs da{k, v, Wk, Wv, S, beta, iB, iH, iL, fp.chunk, fp.nchunk, ws_ds};
     if ((e = timed("attn_partial", s, [&] { return arl2::launch_attn_partial_bf16(aa, s); })))
       return hip_status(e, fn);
     if ((e = timed(update_flag ? "combine_delta" : "combine", s, [&] {

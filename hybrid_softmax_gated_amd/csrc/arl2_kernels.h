@@ -23,7 +23,6 @@ struct AttnPlan {
 constexpr int kQBlock = 128;      // queries per attention workgroup
 constexpr int kKeyTile = 64;      // keys per LDS tile
 constexpr int kMaxSplit = 8;      // most key ranges one attention call is cut into
-constexpr int kDeltaChunk = 128;  // tokens per delta-update workgroup (MFMA path)
 constexpr int kGenChunk = 32;     // tokens per delta-update workgroup (generic path)
 
 AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk);
@@ -65,9 +64,16 @@ struct DeltaArgs {
   const void *Wk, *Wv;   // [H][128][128]
   const float *S;        // [B][H][128][128] (pre-update, read only)
   const float *beta;     // [B][L][H]
-  int B, H, L, nchunk;
+  int B, H, L;
+  int chunk, nchunk;     // tokens per chunk (delta_chunk_tokens), chunks per frame
   float *ws_dS;          // [B][H][nchunk][128][128]
 };
+
+// Tokens per delta-update workgroup for a frame of B x H x L: 96 when the
+// clean pass's delta chunks and combine items then fit in one round of two
+// workgroups per compute unit (shorter items end the launch sooner), else
+// 128 (fewer chunk contributions to write and sum).
+int delta_chunk_tokens(int64_t B, int64_t H, int64_t L);
 
 // One launch for the combine and, when `d` is not null, the delta chunks:
 // both only read S, so they run side by side.

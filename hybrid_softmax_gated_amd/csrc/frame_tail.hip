@@ -543,8 +543,13 @@ __global__ __launch_bounds__(256) void fill_state_kernel(float *dst, const float
 
 }  // namespace
 
+int delta_chunk_tokens(int64_t B, int64_t H, int64_t L) {
+  const int64_t items = B * H * ((L + 95) / 96 + (L + kQBlock - 1) / kQBlock);
+  return items <= 512 ? 96 : 128;
+}
+
 hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_t s) {
-  static_assert(kDeltaChunk % 32 == 0 && kDeltaChunk <= 128, "delta chunk");
+  if (d && d->chunk != 96 && d->chunk != 128) return hipErrorInvalidValue;
   TailKParams P;
   P.c.ws_o = (const char *)c.ws_o;
   P.c.ws_ml = c.ws_ml;
@@ -578,7 +583,10 @@ hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_
     P.delta_blocks = 8 * P.per_xcd_d;
   }
   const unsigned blocks = (unsigned)(P.delta_blocks + 8 * P.per_xcd_c);
-  hipLaunchKernelGGL(tail_kernel<kDeltaChunk / 32>, dim3(blocks), dim3(256), 0, s, P);
+  if (d && d->chunk == 96)
+    hipLaunchKernelGGL(tail_kernel<3>, dim3(blocks), dim3(256), 0, s, P);
+  else
+    hipLaunchKernelGGL(tail_kernel<4>, dim3(blocks), dim3(256), 0, s, P);
   return hipGetLastError();
 }
 

@@ -89,8 +89,10 @@ def _stream(lay, torch, w, frames=None, rows_n=12, out_every=1, until_overflow=F
             out_errs.append((p.frame, out_err_per_head(got, _oracle_rows(q_rows, k, v, W, S_ref))))
         if p.update:
             # the same tensors are alive at every clean pass: the library
-            # itself allocates nothing
-            mem.append(torch.cuda.memory_allocated())
+            # itself allocates nothing. The sum of the live requests is
+            # compared, not the caching allocator's block sizes, which it may
+            # round up by a cached block's unsplit remainder.
+            mem.append(torch.cuda.memory_stats()["requested_bytes.all.current"])
             frame_ms.append(t_frame)
             t_frame = 0.0
             oracle_state_update(S_ref, k, v, W, p.alpha.cpu().numpy(), p.beta.cpu().numpy())

@@ -23,9 +23,11 @@
  * of a frame updates it (clean-pass updates).
  *
  * Conventions for every entry point:
- *  - All tensor pointers are DEVICE pointers owned by the caller; the
- *    library never allocates device memory, never frees caller memory and
- *    keeps no pointer beyond the arl2_state descriptor the caller owns.
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The
+ *    layer's entry points never allocate device memory (only the measurement
+ *    call arl2_profile_mfma_peak takes and frees a small buffer of its own);
+ *    the library never frees caller memory and keeps no pointer beyond the
+ *    arl2_state descriptor the caller owns.
  *  - Activations use token-major layout [B][L][H][d], contiguous.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued asynchronously; kernel faults surface at the caller's

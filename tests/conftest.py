@@ -16,3 +16,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def repo_root():
     return ROOT
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Host time the float64 oracle took in the parity tests, per workload."""
+    pu = sys.modules.get("parity_utils")
+    if pu is None or not pu.ORACLE_SECONDS:
+        return
+    terminalreporter.write_sep("-", f"oracle wall time in the parity tests ({pu.oracle_threads()})")
+    for name, sec in sorted(pu.ORACLE_SECONDS.items()):
+        terminalreporter.write_line(f"oracle {name}: {sec * 1e3:.1f} ms")

@@ -1,6 +1,10 @@
 """Helpers shared by the GPU parity tests (not a test module)."""
 from __future__ import annotations
 
+import contextlib
+import os
+import time
+
 import numpy as np
 
 import oracle as O
@@ -85,3 +89,26 @@ def sample_rows(L: int, n: int, seed: int) -> np.ndarray:
     fixed = {0, L - 1, min(L - 1, 127), min(L - 1, 128), (L - 1) // 128 * 128}
     extra = r.choice(L, size=min(L, n), replace=False)
     return np.array(sorted(fixed | set(int(x) for x in extra)))
+
+
+# Host wall time the float64 oracle spends per workload in the parity tests,
+# with the threads it ran on; the session summary prints it (conftest.py).
+ORACLE_SECONDS: dict = {}
+
+
+@contextlib.contextmanager
+def oracle_clock(workload: str):
+    t0 = time.perf_counter()
+    try:
+        yield
+    finally:
+        ORACLE_SECONDS[workload] = ORACLE_SECONDS.get(workload, 0.0) + time.perf_counter() - t0
+
+
+def oracle_threads() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        n = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl is optional
+        n = None
+    return f"BLAS threads {n}, os.cpu_count() {os.cpu_count()}"

@@ -12,9 +12,9 @@ import pytest
 
 import oracle as O
 import synth_inputs as SI
-from parity_utils import (TOL_OUT, TOL_S, device, oracle_rows, oracle_state_update,
-                          out_err_per_head, rel_max_err, sample_rows, state_err, to_dev,
-                          to_host)
+from parity_utils import (TOL_OUT, TOL_S, device, oracle_clock, oracle_rows,
+                          oracle_state_update, out_err_per_head, rel_max_err, sample_rows,
+                          state_err, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,8 @@ def _run_stream(lay, torch, w, frames=None, S0=None, check_every_pass=True):
         al = torch.from_numpy(p.alpha).to(device())
         be = torch.from_numpy(p.beta).to(device())
         L.forward(q, k, v, Wd, al, be, out, p.update, gate=w.gate)
-        ref = O.frame_forward(p.q, p.k, p.v, W, S_ref, p.alpha, p.beta, int(p.update))
+        with oracle_clock(w.name):
+            ref = O.frame_forward(p.q, p.k, p.v, W, S_ref, p.alpha, p.beta, int(p.update))
         torch.cuda.synchronize()
         if check_every_pass or p.update:
             errs_out.append(out_err_per_head(to_host(out), ref))

@@ -22,8 +22,8 @@ import pytest
 
 import oracle as O
 import synth_inputs as SI
-from parity_utils import (TOL_OUT, TOL_S, device, oracle_state_update, out_err_per_head,
-                          sample_rows, state_err, to_dev, to_host)
+from parity_utils import (TOL_OUT, TOL_S, device, oracle_clock, oracle_state_update,
+                          out_err_per_head, sample_rows, state_err, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,7 +86,9 @@ def _stream(lay, torch, w, frames=None, rows_n=12, out_every=1, until_overflow=F
         if check_out:
             q_rows = p.q.index_select(1, rows_t).float().cpu().numpy()
             got = out.index_select(1, rows_t).float().cpu().numpy().astype(np.float64)
-            out_errs.append((p.frame, out_err_per_head(got, _oracle_rows(q_rows, k, v, W, S_ref))))
+            with oracle_clock(w.name):
+                ref_rows = _oracle_rows(q_rows, k, v, W, S_ref)
+            out_errs.append((p.frame, out_err_per_head(got, ref_rows)))
         if p.update:
             # the same tensors are alive at every clean pass: the library
             # itself allocates nothing. The sum of the live requests is
@@ -95,7 +97,9 @@ def _stream(lay, torch, w, frames=None, rows_n=12, out_every=1, until_overflow=F
             mem.append(torch.cuda.memory_stats()["requested_bytes.all.current"])
             frame_ms.append(t_frame)
             t_frame = 0.0
-            oracle_state_update(S_ref, k, v, W, p.alpha.cpu().numpy(), p.beta.cpu().numpy())
+            alpha_h, beta_h = p.alpha.cpu().numpy(), p.beta.cpu().numpy()
+            with oracle_clock(w.name):
+                oracle_state_update(S_ref, k, v, W, alpha_h, beta_h)
             S_gpu = to_host(layer.S)
             rec = {"frame": p.frame, "ref_finite": bool(np.max(np.abs(S_ref)) < FP32_MAX),
                    "gpu_finite": bool(np.all(np.isfinite(S_gpu))),

@@ -14,7 +14,9 @@ finite over thousands of back-to-back frames; the work does not depend on the
 values). A set of distinct frames is drawn on the GPU before timing and
 cycled; everything is resident in HBM when the timed region starts.
 
-Prints one JSON line (the driver's contract) with, besides frames/s:
+Prints one JSON line with, besides frames/s:
+  frame_latency median, 10th and 90th percentile of 200 frames each timed with
+                its own pair of HIP events, after 10 warm-up frames;
   roofline      the dominant kernel (intra-frame attention) against the bf16
                 dense MFMA peak, from its average launch duration measured
                 with HIP events on its launch stream (arl2_profile_*) in a
@@ -537,6 +539,24 @@ def main() -> int:
     fps = args.steps / wall
     assert torch.isfinite(layer.S).all(), "state went non-finite during the benchmark"
 
+    # ---- per-frame latency: HIP events around each frame (eager), after 10
+    # warm-up frames; the median of 200 frames
+    for i in range(10):
+        step(i)
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(200)]
+    for i, (e0, e1) in enumerate(fev):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_frame = sorted(e0.elapsed_time(e1) for e0, e1 in fev)
+    frame_latency = {"median_ms": round(per_frame[len(per_frame) // 2], 5),
+                     "p10_ms": round(per_frame[len(per_frame) // 10], 5),
+                     "p90_ms": round(per_frame[(9 * len(per_frame)) // 10], 5),
+                     "frames": len(per_frame), "warmup": 10,
+                     "timing": "HIP events around each frame's passes, eager launches"}
+
     # ---- per-kernel durations with HIP events on the launch stream
     Bd.arl2_profile_reset()
     Bd.arl2_profile_enable(True, args.profile_repeat)
@@ -585,6 +605,7 @@ def main() -> int:
         "tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "gflop_per_frame": round(frame_flops / 1e9, 3),
         "event_ms_per_step": round(ev_ms / args.steps, 5),
+        "frame_latency": frame_latency,
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": roofline,
         "mfma_loop_peak_tflops": round(mfma_loop, 1),

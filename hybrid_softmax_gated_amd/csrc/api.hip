@@ -354,6 +354,10 @@ arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, con
     const Range r_a = range(alpha, abytes), r_b = range(beta, (size_t)B * L * H * 4);
     if (overlap(r_a, r_S) || overlap(r_b, r_S) || overlap(r_a, r_ws) || overlap(r_b, r_ws))
       return fail(ARL2_ERR_INVALID_ARG, "%s: alpha/beta overlap the state or its workspace", fn);
+    // The output is written in the launch whose update items read beta, and
+    // before the launch that reads alpha: an overlap would corrupt S.
+    if (overlap(r_out, r_a) || overlap(r_out, r_b))
+      return fail(ARL2_ERR_INVALID_ARG, "%s: out overlaps alpha/beta", fn);
   }
 
   hipStream_t s = (hipStream_t)stream;

@@ -106,6 +106,11 @@ ARL2_API size_t arl2_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t L,
 
 /*
  * Bind a state to caller-owned device memory and set S := 0.
+ * The state is the fixed-size d_k x d_v matrix per stream and head that the
+ * inter-frame branch carries from frame to frame ("Technical Summary ...",
+ * section 2.2 "Memory State Management": its size does not grow with the
+ * number of frames, which is where the constant memory of section 4 comes
+ * from); a new stream starts from the empty memory S = 0.
  *   S_dev   device [B][H][d][d] float32, 16-byte aligned.
  *   ws_dev  device workspace of at least arl2_workspace_bytes(...) bytes,
  *           256-byte aligned (may be NULL only if that size is 0).
@@ -120,12 +125,23 @@ ARL2_API arl2_status arl2_state_init(arl2_state *st, int32_t B, int32_t H, int32
 /*
  * Start a new video stream on an initialised state: S := S0 (device,
  * [B][H][d][d] float32, may not alias S), or S := 0 when S0_dev is NULL.
- * Restoring a saved S this way resumes a stream exactly where it was.
+ * Restoring a saved S this way resumes a stream exactly where it was: the
+ * state is all the inter-frame branch remembers of earlier frames
+ * ("Technical Summary ...", section 2.2), so S plus the next frame's
+ * inputs determine everything that follows.
+ * Errors: INVALID_ARG for a state not set up by arl2_state_init, or an S0
+ * that is misaligned (4 bytes) or overlaps S; ARL2_ERR_HIP if the copy
+ * kernel cannot be launched.
  */
 ARL2_API arl2_status arl2_state_reset(arl2_state *st, const float *S0_dev, void *stream);
 
 /*
- * One pass of one frame through the layer.
+ * One pass of one frame through the layer ("Technical Summary ...", section
+ * 2.1 "Hybrid Attention Decomposition": out = softmax attention inside the
+ * frame + Q' S_{N-1}; section 2.2 "Memory State Management": every token of
+ * the frame reads the same pre-update state, and only the final clean pass
+ * of a frame writes S_N = alpha S_{N-1} + K'^T diag(beta) (V' - K' S_{N-1}),
+ * so the denoising passes in between leave S untouched).
  *   q, k, v  device [B][L][H][d], io dtype, 16-byte aligned, not aliasing out.
  *   Wphi     device [3][H][d][d], io dtype: the maps for q, k, v; map[m][h]
  *            is stored [d_in][d_out] and applied as x' = x W.
@@ -141,8 +157,10 @@ ARL2_API arl2_status arl2_state_reset(arl2_state *st, const float *S0_dev, void 
  *               1 = clean pass: out is computed from the pre-update S, then
  *                   S is updated in place, in stream order.
  * Errors: INVALID_ARG for NULL/misaligned pointers, aliasing of out with an
- * input, update_flag not in {0, 1}, NULL alpha/beta with update_flag == 1,
- * or an uninitialised state; ARL2_ERR_HIP if a launch fails.
+ * input, the state or its workspace (and, when update_flag == 1, with alpha
+ * or beta), inputs overlapping the state or its workspace, update_flag not
+ * in {0, 1}, NULL alpha/beta with update_flag == 1, or an uninitialised
+ * state; ARL2_ERR_HIP if a launch fails.
  */
 ARL2_API arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, const void *Wphi,
                                arl2_state *st, const float *alpha, const float *beta,

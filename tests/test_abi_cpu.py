@@ -166,6 +166,10 @@ def test_frame_forward_validation(B):
     assert _code(B.arl2_frame_forward, FAKE_S, K, V, W, st, AL, BE, OUT, 1)[0] == E
     # beta overlapping the state
     assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL, FAKE_S, OUT, 1)[0] == E
+    # out overlapping alpha or beta on a clean pass (the update reads both
+    # after or while out is written)
+    assert "alpha/beta" in _code(B.arl2_frame_forward, Q, K, V, W, st, OUT + 64, BE, OUT, 1)[1]
+    assert "alpha/beta" in _code(B.arl2_frame_forward, Q, K, V, W, st, AL, OUT + 512, OUT, 1)[1]
     # a workspace that is too small for the state's shape
     st.ws_bytes -= 256
     assert _code(B.arl2_frame_forward, Q, K, V, W, st, AL, BE, OUT, 0)[0] == E
@@ -184,6 +188,11 @@ def test_gated_frame_forward_validation(B):
     # an elementwise alpha ([B][H][d] floats) that reaches into the state
     assert _code(g, Q, K, V, W, st, FAKE_S - 512, B.ARL2_GATE_ELEMENTWISE, BE, OUT, 1)[0] == E
     assert _code(g, Q, K, V, W, st, AL, B.ARL2_GATE_HEADWISE, BE, OUT, 7)[0] == E
+    # out overlapping the elementwise alpha or beta on a clean pass
+    assert "alpha/beta" in _code(g, Q, K, V, W, st, OUT + 4096, B.ARL2_GATE_ELEMENTWISE, BE,
+                                 OUT, 1)[1]
+    assert "alpha/beta" in _code(g, Q, K, V, W, st, AL, B.ARL2_GATE_ELEMENTWISE, OUT + 16,
+                                 OUT, 1)[1]
 
 
 def test_state_reset_validation(B):

@@ -267,15 +267,15 @@ def stack_report(path, frames, layers=30, ratios=(0.0, 0.5, 0.75), pool=4):
     """An attention-only stack: `layers` self-attention layers per pass, of
     which round(ratio * layers) are this layer and the rest full-softmax
     attention over their own key/value cache (the clean keys/values of every
-    previous frame, then the pass's own), for 4 query-only + 1 clean passes
-    per latent frame. Activations are synthetic and cycled from a small pool
-    (the work does not depend on the values). Per frame: GPU time of all
-    layers and passes (HIP events around the frame) and allocated device
-    memory after the frame."""
+    previous frame, then the pass's own; hybrid_softmax_gated_amd.stack), for
+    4 query-only + 1 clean passes per latent frame. Activations are synthetic
+    and cycled from a small pool (the work does not depend on the values).
+    Per frame: GPU time of all layers and passes (HIP events around the
+    frame) and allocated device memory after the frame."""
     import torch
 
     import synth_inputs as SI
-    from hybrid_softmax_gated_amd.layer import ARL2Layer, softmax_attention
+    from hybrid_softmax_gated_amd.stack import AttentionStack
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -290,35 +290,18 @@ def stack_report(path, frames, layers=30, ratios=(0.0, 0.5, 0.75), pool=4):
     res = {"layers": layers, "frames": frames, "passes_per_frame": npass, "runs": {}}
     for ratio in ratios:
         n_arl2 = int(round(ratio * layers))
-        arl2 = [ARL2Layer(B, H, d, L, 0) for _ in range(n_arl2)]
-        ncache = layers - n_arl2
-        caps = [1] * ncache
-        kcs = [torch.empty((B, L, H, d), dtype=torch.bfloat16, device=dev) for _ in range(ncache)]
-        vcs = [torch.empty_like(k) for k in kcs]
-        run = {"arl2_layers": n_arl2, "softmax_layers": ncache, "ms": [], "allocated": []}
+        stack = AttentionStack(B, H, d, L, layers, n_arl2, device=dev)
+        run = {"arl2_layers": n_arl2, "softmax_layers": layers - n_arl2, "ms": [],
+               "allocated": []}
         for f in range(frames):
-            for c in range(ncache):  # room for this frame's keys/values
-                if f + 1 > caps[c]:
-                    caps[c] *= 2
-                    k2 = torch.empty((B, caps[c] * L, H, d), dtype=torch.bfloat16, device=dev)
-                    v2 = torch.empty_like(k2)
-                    k2[:, :f * L] = kcs[c][:, :f * L]
-                    v2[:, :f * L] = vcs[c][:, :f * L]
-                    kcs[c], vcs[c] = k2, v2
-                    del k2, v2
+            for c in stack.caches:  # room for this frame's keys/values, outside the timing
+                c.reserve(f + 1)
             torch.cuda.synchronize()
             ev[0].record()
             for ps in range(npass):
                 for li in range(layers):
                     p = inputs[((f + li) % pool) * npass + ps]
-                    if li < n_arl2:
-                        arl2[li].forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update)
-                    else:
-                        c = li - n_arl2
-                        kcs[c][:, f * L:(f + 1) * L] = p.k
-                        vcs[c][:, f * L:(f + 1) * L] = p.v
-                        softmax_attention(p.q, kcs[c][:, :(f + 1) * L], vcs[c][:, :(f + 1) * L],
-                                          out, 0)
+                    stack.forward(li, f, p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update)
             ev[1].record()
             torch.cuda.synchronize()
             run["ms"].append(ev[0].elapsed_time(ev[1]))
@@ -327,7 +310,7 @@ def stack_report(path, frames, layers=30, ratios=(0.0, 0.5, 0.75), pool=4):
                 print(f"stack {int(ratio * 100)}% frame {f + 1}: {run['ms'][-1]:.2f} ms, "
                       f"{run['allocated'][-1] / 1e9:.2f} GB", file=sys.stderr, flush=True)
         res["runs"][f"{int(ratio * 100)}%"] = run
-        del arl2, kcs, vcs
+        del stack
         torch.cuda.empty_cache()
     with open(path, "w") as fh:
         json.dump(res, fh)

@@ -55,11 +55,15 @@ def _oracle_rows(q_rows, k, v, W, S):
     return out
 
 
-def _stream(lay, torch, w, frames=None, rows_n=12, out_every=1, until_overflow=False):
+def _stream(lay, torch, w, frames=None, rows_n=12, out_every=1, until_overflow=False,
+            full_at=(), full_errs=None):
     """Runs a workload; returns per-clean-pass records and the output errors.
 
     out_every: compare sampled outputs on every pass (1) or on the first
-    query-only pass and the clean pass of every frame (0)."""
+    query-only pass and the clean pass of every frame (0).
+    full_at: (frame, pass index) pairs, 0-based, whose whole output (every
+    row of every (stream, head)) is compared with the oracle; the worst
+    per-(stream, head) error of each is appended to ``full_errs``."""
     layer = lay.ARL2Layer(w.B, w.H, w.d, w.L, 0)
     W = SI.make_weights(w)
     Wd = to_dev(W, w.dtype)
@@ -80,9 +84,21 @@ def _stream(lay, torch, w, frames=None, rows_n=12, out_every=1, until_overflow=F
         torch.cuda.synchronize()
         t_frame += ev[0].elapsed_time(ev[1])
         check_out = ref_finite and (out_every == 1 or p.index == 0 or p.update)
-        if check_out or p.update:
+        full = ref_finite and (p.frame, p.index) in full_at
+        if check_out or p.update or full:
             k = p.k.float().cpu().numpy()
             v = p.v.float().cpu().numpy()
+        if full:
+            q = p.q.float().cpu().numpy()
+            got_full = to_host(out)
+            ref_full = np.empty_like(got_full)
+            with oracle_clock(w.name + "_full_outputs"):
+                for b in range(w.B):
+                    for h in range(w.H):
+                        ref_full[b, :, h] = O.output_rows(q[b, :, h], k[b, :, h], v[b, :, h],
+                                                          W[0, h], S_ref[b, h], np.arange(w.L))
+            full_errs.append(((p.frame, p.index), out_err_per_head(got_full, ref_full)))
+            del q, got_full, ref_full
         if check_out:
             q_rows = p.q.index_select(1, rows_t).float().cpu().numpy()
             got = out.index_select(1, rows_t).float().cpu().numpy().astype(np.float64)
@@ -236,12 +252,20 @@ def test_maximum_heads_and_streams(lay, torch, Bn, H):
 def test_batched720p(lay, torch):
     """Four independent streams (seeds 0..3) at the 720p latent shape
     (L = 3600), 21 frames of 4 query-only + 1 clean pass; sampled outputs
-    on every pass."""
+    on every pass, and every output row of every (stream, head) on the first
+    query-only pass of frame 1 and the clean passes of frames 1 and 21. This
+    shape's plan differs from 480p's: one key range of 57 tiles per query
+    block, 29 query blocks per head and 128-token update chunks."""
     w = SI.WORKLOADS["batched720p"]
     t0 = time.time()
-    recs, out_errs, _ = _stream(lay, torch, w, rows_n=8)
-    print(f"batched720p took {time.time() - t0:.1f} s")
+    full = []
+    recs, out_errs, _ = _stream(lay, torch, w, rows_n=8, full_at={(0, 0), (0, 4), (20, 4)},
+                                full_errs=full)
+    print(f"batched720p took {time.time() - t0:.1f} s; full outputs (frame, pass): "
+          + ", ".join(f"{fp}: {e:.2e}" for fp, e in full))
     assert len(recs) == 21
+    assert sorted(fp for fp, _ in full) == [(0, 0), (0, 4), (20, 4)]
+    assert max(e for _, e in full) < TOL_OUT[SI.BF16]
     _check(recs, out_errs, w.name)
 
 

@@ -70,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "arl2_frame_forward": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, P, P, I, P]),
         "arl2_frame_forward_gated": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, I, P, P, I,
                                          P]),
+        "arl2_frame_forward_noalloc": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, P, P, I,
+                                           P]),
         "arl2_token_level_workspace_bytes": (Z, [I, I, I, I, I]),
         "arl2_frame_forward_token_level": (I, [P, P, P, P, ctypes.POINTER(arl2_state), P, P, P, I,
                                                P, Z, P]),
@@ -93,6 +95,7 @@ _lib = _load()
 
 EXPORTED = ("arl2_version", "arl2_status_string", "arl2_last_error", "arl2_workspace_bytes",
             "arl2_state_init", "arl2_state_reset", "arl2_frame_forward", "arl2_frame_forward_gated",
+            "arl2_frame_forward_noalloc",
             "arl2_softmax_attention_workspace_bytes", "arl2_softmax_attention",
             "arl2_gate_projections_workspace_bytes", "arl2_gate_projections",
             "arl2_token_level_workspace_bytes", "arl2_frame_forward_token_level",
@@ -165,6 +168,17 @@ def arl2_frame_forward_gated(q, k, v, Wphi, st: arl2_state, alpha, gate: int, be
     _check(_lib.arl2_frame_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(Wphi), ctypes.byref(st),
                                          _ptr(alpha), gate, _ptr(beta), _ptr(out), update_flag,
                                          _stream(stream)))
+
+
+# Bytes of scratch the no-allocation pass holds per device (include/arl2.h).
+ARL2_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def arl2_frame_forward_noalloc(q, k, v, Wphi, st: arl2_state, alpha, beta, out, update_flag: int,
+                               stream=None) -> None:
+    _check(_lib.arl2_frame_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(Wphi),
+                                           ctypes.byref(st), _ptr(alpha), _ptr(beta), _ptr(out),
+                                           update_flag, _stream(stream)))
 
 
 def arl2_token_level_workspace_bytes(B: int, H: int, d: int, L: int, dtype: int) -> int:

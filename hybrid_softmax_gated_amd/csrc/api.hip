@@ -225,6 +225,43 @@ arl2_status hip_status(hipError_t e, const char *what) {
 
 }  // namespace
 
+// Scratch of arl2_frame_forward_noalloc: the pass's workspace (attention
+// partials and update partials), one copy per device, held until the
+// process ends. Host code never uses this name as an address: each
+// device's copy is reached through the address hipGetSymbolAddress gives
+// with that device current (scratch_address below).
+static __device__ __align__(256) char scratch[ARL2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up once per device.
+arl2_status scratch_address(const char *fn, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ARL2_ERR_UNSUPPORTED, "%s: device index %d (at most %d devices)", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!p || !aligned(p, 256))
+      return fail(ARL2_ERR_HIP, "%s: the scratch of device %d has no 256-byte aligned address",
+                  fn, dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ARL2_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t arl2_version(void) { return ARL2_VERSION; }
@@ -256,15 +293,26 @@ arl2_status arl2_state_init(arl2_state *st, int32_t B, int32_t H, int32_t d, int
   if (!aligned(S_dev, 16))
     return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: S_dev is not 16-byte aligned");
   const size_t need = plan_frame(B, H, d, L, dtype).total;
-  if (ws_bytes < need)
+  // No workspace at all (NULL, 0 bytes): the state can only run passes
+  // through arl2_frame_forward_noalloc, whose scratch is the library's own.
+  const bool no_ws = !ws_dev && ws_bytes == 0;
+  if (!no_ws && ws_bytes < need)
     return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: workspace of %zu bytes, need %zu",
                 ws_bytes, need);
-  if (need > 0 && !ws_dev) return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: ws_dev is NULL");
+  if (!no_ws && need > 0 && !ws_dev)
+    return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: ws_dev is NULL");
   if (ws_dev && !aligned(ws_dev, 256))
     return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: ws_dev is not 256-byte aligned");
   const size_t s_bytes = (size_t)B * H * d * d * sizeof(float);
   if (ws_dev && overlap(range(S_dev, s_bytes), range(ws_dev, ws_bytes)))
     return fail(ARL2_ERR_INVALID_ARG, "arl2_state_init: S and workspace overlap");
+  if (no_ws) {
+    // Set-up of a caller that cannot allocate: find this device's scratch
+    // now, so that its passes do not have to.
+    void *p = nullptr;
+    arl2_status ss = scratch_address("arl2_state_init", &p);
+    if (ss != ARL2_OK) return ss;
+  }
   arl2_status hs = hip_status(
       timed("fill_state", (hipStream_t)stream, [&] { return arl2::launch_fill_state(S_dev, nullptr, (int64_t)B * H * d * d, (hipStream_t)stream); }),
       "arl2_state_init");
@@ -285,10 +333,16 @@ static arl2_status check_state(const arl2_state *st, const char *what) {
   if (!st) return fail(ARL2_ERR_INVALID_ARG, "%s: st is NULL", what);
   if (st->magic != kMagic || !st->S)
     return fail(ARL2_ERR_INVALID_ARG, "%s: state was not set up by arl2_state_init", what);
-  arl2_status cs = check_shape(st->B, st->H, st->d, st->L, st->dtype, what);
-  if (cs != ARL2_OK) return cs;
+  return check_shape(st->B, st->H, st->d, st->L, st->dtype, what);
+}
+
+// The state's own workspace must hold the frame plan (passes other than
+// arl2_frame_forward_noalloc use it).
+static arl2_status check_state_ws(const arl2_state *st, const char *what) {
   if (st->ws_bytes < plan_frame(st->B, st->H, st->d, st->L, st->dtype).total)
-    return fail(ARL2_ERR_INVALID_ARG, "%s: workspace too small for the state's shape", what);
+    return fail(ARL2_ERR_INVALID_ARG,
+                "%s: the state's workspace is too small for its shape (a state bound without "
+                "a workspace runs passes through arl2_frame_forward_noalloc only)", what);
   return ARL2_OK;
 }
 
@@ -310,12 +364,13 @@ arl2_status arl2_state_reset(arl2_state *st, const float *S0_dev, void *stream) 
 
 namespace {
 
-arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, const void *v,
-                               const void *Wphi, arl2_state *st, const float *alpha,
-                               int32_t gate, const float *beta, void *out, int32_t update_flag,
-                               void *stream) {
-  arl2_status cs = check_state(st, fn);
-  if (cs != ARL2_OK) return cs;
+// Argument checks of one pass whose workspace is `ws_base`, `ws_cap` bytes
+// (the state's own, or the no-allocation scratch; an empty range when that
+// is not known yet). No HIP call.
+arl2_status check_frame_args(const char *fn, const void *q, const void *k, const void *v,
+                             const void *Wphi, const arl2_state *st, const float *alpha,
+                             int32_t gate, const float *beta, const void *out,
+                             int32_t update_flag, const void *ws_base, size_t ws_cap) {
   if (update_flag != 0 && update_flag != 1)
     return fail(ARL2_ERR_INVALID_ARG, "%s: update_flag %d is not 0 or 1", fn, update_flag);
   if (gate != ARL2_GATE_HEADWISE && gate != ARL2_GATE_ELEMENTWISE)
@@ -332,8 +387,7 @@ arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, con
   const size_t act = (size_t)B * L * H * d * es;
   const size_t wbytes = (size_t)3 * H * d * d * es;
   const size_t sbytes = (size_t)B * H * d * d * sizeof(float);
-  const Range r_out = range(out, act), r_S = range(st->S, sbytes),
-              r_ws = range(st->ws, st->ws_bytes);
+  const Range r_out = range(out, act), r_S = range(st->S, sbytes), r_ws = range(ws_base, ws_cap);
   const Range r_in[4] = {range(q, act), range(k, act), range(v, act), range(Wphi, wbytes)};
   for (int i = 0; i < 4; ++i)
     if (overlap(r_out, r_in[i]))
@@ -359,10 +413,23 @@ arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, con
     if (overlap(r_out, r_a) || overlap(r_out, r_b))
       return fail(ARL2_ERR_INVALID_ARG, "%s: out overlaps alpha/beta", fn);
   }
+  return ARL2_OK;
+}
 
+// One pass with the workspace `ws_base` of `ws_cap` bytes (the state's own,
+// or the no-allocation scratch).
+arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, const void *v,
+                               const void *Wphi, arl2_state *st, const float *alpha,
+                               int32_t gate, const float *beta, void *out, int32_t update_flag,
+                               void *ws_base, size_t ws_cap, void *stream) {
+  arl2_status cs = check_frame_args(fn, q, k, v, Wphi, st, alpha, gate, beta, out, update_flag,
+                                    ws_base, ws_cap);
+  if (cs != ARL2_OK) return cs;
+  const int64_t B = st->B, H = st->H, d = st->d, L = st->L;
+  const size_t es = esize(st->dtype);
   hipStream_t s = (hipStream_t)stream;
   const FramePlan fp = plan_frame(B, H, d, L, st->dtype);
-  char *ws = (char *)st->ws;
+  char *ws = (char *)ws_base;
   float *ws_o = (float *)(ws + fp.off_o);
   float *ws_ml = (float *)(ws + fp.off_ml);
   float *ws_ds = (float *)(ws + fp.off_ds);
@@ -417,16 +484,47 @@ arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, con
 arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, const void *Wphi,
                                arl2_state *st, const float *alpha, const float *beta, void *out,
                                int32_t update_flag, void *stream) {
-  return frame_forward_impl("arl2_frame_forward", q, k, v, Wphi, st, alpha, ARL2_GATE_HEADWISE,
-                            beta, out, update_flag, stream);
+  const char *fn = "arl2_frame_forward";
+  arl2_status cs = check_state(st, fn);
+  if (cs == ARL2_OK) cs = check_state_ws(st, fn);
+  if (cs != ARL2_OK) return cs;
+  return frame_forward_impl(fn, q, k, v, Wphi, st, alpha, ARL2_GATE_HEADWISE, beta, out,
+                            update_flag, st->ws, st->ws_bytes, stream);
 }
 
 arl2_status arl2_frame_forward_gated(const void *q, const void *k, const void *v,
                                      const void *Wphi, arl2_state *st, const float *alpha,
                                      int32_t gate, const float *beta, void *out,
                                      int32_t update_flag, void *stream) {
-  return frame_forward_impl("arl2_frame_forward_gated", q, k, v, Wphi, st, alpha, gate, beta,
-                            out, update_flag, stream);
+  const char *fn = "arl2_frame_forward_gated";
+  arl2_status cs = check_state(st, fn);
+  if (cs == ARL2_OK) cs = check_state_ws(st, fn);
+  if (cs != ARL2_OK) return cs;
+  return frame_forward_impl(fn, q, k, v, Wphi, st, alpha, gate, beta, out, update_flag, st->ws,
+                            st->ws_bytes, stream);
+}
+
+arl2_status arl2_frame_forward_noalloc(const void *q, const void *k, const void *v,
+                                       const void *Wphi, arl2_state *st, const float *alpha,
+                                       const float *beta, void *out, int32_t update_flag,
+                                       void *stream) {
+  const char *fn = "arl2_frame_forward_noalloc";
+  arl2_status cs = check_state(st, fn);
+  if (cs != ARL2_OK) return cs;
+  const size_t need = plan_frame(st->B, st->H, st->d, st->L, st->dtype).total;
+  if (need > ARL2_NOALLOC_SCRATCH_BYTES)
+    return fail(ARL2_ERR_INVALID_ARG,
+                "%s: this shape needs %zu bytes of scratch; the no-allocation pass holds at most "
+                "%zu (B=%d H=%d d=%d L=%d): use arl2_frame_forward with a workspace",
+                fn, need, (size_t)ARL2_NOALLOC_SCRATCH_BYTES, st->B, st->H, st->d, st->L);
+  cs = check_frame_args(fn, q, k, v, Wphi, st, alpha, ARL2_GATE_HEADWISE, beta, out,
+                        update_flag, nullptr, 0);
+  if (cs != ARL2_OK) return cs;
+  void *scr = nullptr;
+  cs = scratch_address(fn, &scr);
+  if (cs != ARL2_OK) return cs;
+  return frame_forward_impl(fn, q, k, v, Wphi, st, alpha, ARL2_GATE_HEADWISE, beta, out,
+                            update_flag, scr, ARL2_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 namespace {
@@ -458,6 +556,7 @@ arl2_status arl2_frame_forward_token_level(const void *q, const void *k, const v
                                            void *tl_ws, size_t tl_ws_bytes, void *stream) {
   const char *fn = "arl2_frame_forward_token_level";
   arl2_status cs = check_state(st, fn);
+  if (cs == ARL2_OK) cs = check_state_ws(st, fn);
   if (cs != ARL2_OK) return cs;
   if (update_flag != 0 && update_flag != 1)
     return fail(ARL2_ERR_INVALID_ARG, "%s: update_flag %d is not 0 or 1", fn, update_flag);

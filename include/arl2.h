@@ -113,7 +113,9 @@ ARL2_API size_t arl2_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t L,
  * from); a new stream starts from the empty memory S = 0.
  *   S_dev   device [B][H][d][d] float32, 16-byte aligned.
  *   ws_dev  device workspace of at least arl2_workspace_bytes(...) bytes,
- *           256-byte aligned (may be NULL only if that size is 0).
+ *           256-byte aligned; or NULL with ws_bytes == 0 for a state whose
+ *           passes all go through arl2_frame_forward_noalloc (the other
+ *           pass entry points then return INVALID_ARG for it).
  * The zero fill is enqueued on `stream`.
  * Errors: INVALID_ARG for NULL st/S_dev, a bad shape, a too-small or
  * misaligned workspace; UNSUPPORTED for d not in {16, 128}.
@@ -165,6 +167,32 @@ ARL2_API arl2_status arl2_state_reset(arl2_state *st, const float *S0_dev, void 
 ARL2_API arl2_status arl2_frame_forward(const void *q, const void *k, const void *v, const void *Wphi,
                                arl2_state *st, const float *alpha, const float *beta,
                                void *out, int32_t update_flag, void *stream);
+
+/*
+ * arl2_frame_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). The pass's partial results live
+ * in a scratch array of ARL2_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each device it runs on until the process ends; the call allocates
+ * nothing and frees nothing. The state may have been bound with or without
+ * a workspace (arl2_state_init); its own workspace is not used.
+ *   Arguments, layout, ownership and results are those of
+ *   arl2_frame_forward (headwise gate).
+ * Every call on one device shares that device's scratch: calls that may
+ * overlap in time on one device (different streams, or different host
+ * threads without ordering) race on it and must be ordered by the caller.
+ * The scratch keeps the last call's contents; nothing in it needs to start
+ * at zero.
+ * Errors: those of arl2_frame_forward; INVALID_ARG also when the state's
+ * shape needs more than ARL2_NOALLOC_SCRATCH_BYTES of scratch
+ * (arl2_workspace_bytes tells how much it needs); ARL2_ERR_HIP if the
+ * scratch's device address cannot be found.
+ */
+#define ARL2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ARL2_API arl2_status arl2_frame_forward_noalloc(const void *q, const void *k, const void *v,
+                                                const void *Wphi, arl2_state *st,
+                                                const float *alpha, const float *beta, void *out,
+                                                int32_t update_flag, void *stream);
 
 /* Forget-gate kinds of arl2_frame_forward_gated. */
 typedef enum {

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert {"arl2_state_init", "arl2_state_reset", "arl2_frame_forward",
             "arl2_frame_forward_gated", "arl2_workspace_bytes"} <= names
-    assert len(names) == 18
+    assert len(names) == 19
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -193,6 +193,31 @@ def test_gated_frame_forward_validation(B):
                                  OUT, 1)[1]
     assert "alpha/beta" in _code(g, Q, K, V, W, st, AL, B.ARL2_GATE_ELEMENTWISE, OUT + 16,
                                  OUT, 1)[1]
+
+
+def test_noalloc_pass_validation(B):
+    """The no-allocation pass validates like arl2_frame_forward and rejects a
+    shape whose scratch need exceeds the library's array, before any HIP
+    call; a state bound without a workspace is refused by the other passes."""
+    E = B.ARL2_ERR_INVALID_ARG
+    f = B.arl2_frame_forward_noalloc
+    import re as _re
+    hdr = open(HEADER).read()
+    m = _re.search(r"#define ARL2_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.ARL2_NOALLOC_SCRATCH_BYTES
+    # the 480p frame step fits; batched 720p does not
+    assert B.arl2_workspace_bytes(1, 12, 128, 1560, 0) <= B.ARL2_NOALLOC_SCRATCH_BYTES
+    big = _fake_state(B, Bn=4, H=12, L=3600)
+    assert B.arl2_workspace_bytes(4, 12, 128, 3600, 0) > B.ARL2_NOALLOC_SCRATCH_BYTES
+    code, msg = _code(f, Q, K, V, W, big, AL, BE, OUT, 1)
+    assert code == E and "scratch" in msg
+    st = _fake_state(B)
+    assert _code(f, Q, K, V, W, B.arl2_state(), AL, BE, OUT, 1)[0] == E
+    assert _code(f, Q, K, V, W, st, AL, BE, OUT, 3)[0] == E
+    # a state without a workspace: only the no-allocation pass accepts it
+    st.ws, st.ws_bytes = None, 0
+    assert "noalloc" in _code(B.arl2_frame_forward, Q, K, V, W, st, AL, BE, OUT, 0)[1]
+    assert "noalloc" in _code(B.arl2_frame_forward_gated, Q, K, V, W, st, AL, 0, BE, OUT, 0)[1]
 
 
 def test_state_reset_validation(B):

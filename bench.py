@@ -2,11 +2,13 @@
 """Throughput of one ARL2 hybrid attention layer on one MI355X.
 
 One step = one latent frame through one layer: every pass of the frame (the
-query-only denoising pass(es), then the clean pass that updates the state),
+query-only denoising passes, then the clean pass that updates the state),
 i.e. every step of the hot path: intra-frame softmax attention, feature maps
 with L2 norms, the frame-level read of the state, the combine, and the gated
-delta update. Default workload: the Wan2.1-1.3B 480p frame step (B=1, 12
-heads of 128, L=1560 tokens, 1 query-only + 1 clean pass per frame).
+delta update. Default workload: the 21-frame stream's schedule at the
+Wan2.1-1.3B 480p shape (B=1, 12 heads of 128, L=1560 tokens, 4 query-only +
+1 clean pass per frame); the same line also carries the 1 + 1 schedule of
+the single 480p frame step (`frame_step_1p1`).
 
 Inputs are synthetic and seeded (q, k, v ~ N(0,1) in bf16, W = I + N(0,0.01),
 alpha = sigmoid(N(2,0.5)), beta = sigmoid(N(0,1)) / L so that the state stays
@@ -15,20 +17,27 @@ values). A set of distinct frames is drawn on the GPU before timing and
 cycled; everything is resident in HBM when the timed region starts.
 
 Prints one JSON line with, besides frames/s:
-  frame_latency median, 10th and 90th percentile of 200 frames each timed with
-                its own pair of HIP events, after 10 warm-up frames;
-  roofline      the dominant kernel (intra-frame attention) against the bf16
-                dense MFMA peak, from its average launch duration measured
-                with HIP events on its launch stream (arl2_profile_*) in a
-                leg after the timed region, each idempotent kernel launched
-                --profile-repeat times back to back per event pair;
+  frame_latency  median, 10th and 90th percentile of 200 frames each timed
+                 with its own pair of HIP events, after 10 warm-up frames;
+  kernels_us     per launch kind, in sequence: HIP events taken from the
+                 kernels' own start and end (arl2_profile_enable with
+                 repeat 1); kernels_us_warm: the same launches repeated 10
+                 times back to back between two event markers;
+  roofline       the dominant kernel (intra-frame attention, the query-only
+                 pass's first launch) against the bf16 dense MFMA peak, from
+                 its in-sequence launch time; `traffic` is the HBM bytes per
+                 launch from the committed rocprofv3 counter summary when it
+                 was taken on the current kernel source, else null;
+  delta_update   the gated delta update's algorithmic flops over the time its
+                 chunks add to the launch they share with the attention;
+  epilogues      the memory-bound second launches against the HBM peak,
+                 priced by the method's own bytes (inputs read once, outputs
+                 written once; the design's scratch reported beside them);
   mfma_loop_peak_tflops  the bf16 MFMA rate a pure matrix-core loop sustains
-                on this device in the same run (arl2_profile_mfma_peak), the
-                measured counterpart of the published peak; roofline.frac
-                stays against the published peak;
-  cpu_baseline  the float64 oracle on this host's cores, on a bounded sample
-                (frames/s, and GFLOP/s on the same flop count as the GPU figure;
-                cores = the BLAS threads it used).
+                 on this device in the same run (arl2_profile_mfma_peak);
+  cpu_baseline   the float64 oracle on this host's cores, on a bounded sample
+                 (frames/s, and GFLOP/s on the same flop count as the GPU
+                 figure; cores = the BLAS threads it used).
 """
 from __future__ import annotations
 
@@ -79,12 +88,13 @@ def measured_traffic(kernel, workload, digest):
 
 
 def workspace_parts(B, H, d, L):
-    """Bytes of the key-range partials (bf16 O/l, then fp32 max and sum per
-    query) and of the delta chunks' fp32 d x d contributions that one pass of
-    the bf16 d = 128 path keeps between its launches. The key-range count
-    follows the attention plan (two workgroups per CU, at least two 64-key
-    tiles per range, at most 8 ranges); the chunks hold 96 tokens when the
-    delta chunks and the combine's query blocks fit 512 workgroups, else 128."""
+    """Bytes of the workspace regions one pass of the bf16 d = 128 path keeps
+    between its launches: the key-range partials (bf16 O/l, then fp32 max
+    and sum per query), the delta chunks' fp32 d x d contributions, and the
+    bf16 copy of the state. The key-range count follows the attention plan
+    (two workgroups per CU, at least two 64-key tiles per range, at most 8
+    ranges); the chunks hold 96 tokens when the delta chunks and the
+    combine's query blocks fit 512 workgroups, else 128."""
     nqblk = -(-L // 128)
     base = B * H * nqblk
     ns = max(1, min(512 // base, -(-L // 128), 8))
@@ -93,21 +103,28 @@ def workspace_parts(B, H, d, L):
     blocks = B * H * nqblk * nsplit
     chunk = 96 if B * H * (-(-L // 96) + nqblk) <= 512 else 128
     nchunk = -(-L // chunk)
-    return blocks * 128 * d * 2, blocks * 128 * 2 * 4, B * H * nchunk * d * d * 4
+    return (blocks * 128 * d * 2, blocks * 128 * 2 * 4, B * H * nchunk * d * d * 4,
+            B * H * d * d * 2)
 
 
-def epilogue_bytes(B, H, d, L):
-    """Bytes each memory-bound launch of a pass must move (each input read
-    once, each output written once) on the bf16 d = 128 path: the combine
-    reads the key-range partials, q, S and W_q and writes out; the delta
-    chunks read k, v, W_k, W_v, S and beta and write their contributions;
-    delta_apply reads those and S and writes S."""
-    o_bytes, ml_bytes, ds = workspace_parts(B, H, d, L)
+def method_bytes(B, H, d, L):
+    """Bytes each launch of a pass must move by the method's definition
+    (each input read once, each output written once), and the scratch the
+    design moves besides (written by the first launch, read by the second).
+    First launch: q, k, v (and, clean pass, W_k, W_v, S, beta for the delta
+    chunks). Second launch: the inter-frame read and the output, q, W_q, S,
+    out (and, clean pass, S read and written by the update, alpha)."""
+    o_bytes, ml_bytes, ds, s16 = workspace_parts(B, H, d, L)
     io = B * L * H * d * 2
     state = B * H * d * d * 4
-    combine = o_bytes + ml_bytes + io + state + H * d * d * 2 + io
-    delta = 2 * io + 2 * H * d * d * 2 + state + B * L * H * 4 + ds
-    return {"combine": combine, "combine_delta": combine + delta, "delta_apply": ds + 2 * state}
+    w = H * d * d * 2
+    combine = io + w + state + io
+    return {"attn_partial": {"method": 3 * io, "scratch": o_bytes + ml_bytes + s16},
+            "attn_delta": {"method": 3 * io + 2 * w + state + B * L * H * 4,
+                           "scratch": o_bytes + ml_bytes + s16 + ds},
+            "combine": {"method": combine, "scratch": o_bytes + ml_bytes + s16},
+            "combine_apply": {"method": combine + 2 * state + B * H * 4,
+                              "scratch": o_bytes + ml_bytes + s16 + ds}}
 
 
 def cpu_baseline(frames_host, W, w, budget_s=15.0, max_frames=400, access="frame"):
@@ -380,7 +397,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="frame_step_480p",
+    ap.add_argument("--workload", default="stream21_480p",
                     choices=["frame_step_480p", "stream21_480p", "batched720p"])
     ap.add_argument("--gate", default="headwise", choices=["headwise", "elementwise"],
                     help="forget gate: one scalar per head (the method's) or one value per "
@@ -441,7 +458,6 @@ def main() -> int:
 
     import synth_inputs as SI
     from hybrid_softmax_gated_amd import binding as Bd
-    from hybrid_softmax_gated_amd.layer import ARL2Layer
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -461,47 +477,163 @@ def main() -> int:
         print(json.dumps({"workload": w.name, "gate_projections": leg}), flush=True)
         return 0
 
-    # ---- inputs, resident in HBM before timing
-    W = SI.make_weights(w)
-    Wd = torch.from_numpy(W).to(dev).to(torch.bfloat16)
-    frames = []
-    gen = SI.iter_passes_device(w, dev, frames=NUM_DISTINCT_FRAMES)
-    cur = []
-    for p in gen:
+    stream = torch.cuda.current_stream()
+    main_leg = time_schedule(w, dev, stream, args.steps, args.warmup, args.access,
+                             graph=args.graph, profile_steps=args.profile_steps,
+                             profile_repeat=args.profile_repeat)
+    if main_leg is None:
+        return 2
+    fps = main_leg["fps"]
+    kern_us = main_leg["kernels_us"]
+
+    # The single 480p frame step's 1 + 1 schedule, a shorter timed leg.
+    extra = None
+    if args.workload != "frame_step_480p" and args.access == "frame" and args.gate == "headwise":
+        w11 = SI.companion(SI.WORKLOADS["frame_step_480p"])
+        leg = time_schedule(w11, dev, stream, max(200, args.steps // 2), args.warmup, "frame",
+                            profile_steps=max(20, args.profile_steps // 2), profile_repeat=1)
+        fa11, fb11, fc11 = flops(w11.B, w11.H, w11.d, w11.L)
+        extra = {"workload": w11.name, "passes_per_frame": "1 query-only + 1 clean",
+                 "value": round(leg["fps"], 2), "unit": "frames/s",
+                 "ms_per_step": round(1000.0 / leg["fps"], 5),
+                 "tflops": round((2 * (fa11 + fb11) + fc11) * leg["fps"] / 1e12, 2),
+                 "kernels_us": {k: round(v, 2) for k, v in leg["kernels_us"].items()},
+                 "frame_latency": leg["frame_latency"]}
+
+    gate_leg = gate_projection_leg(w, dev, stream, 20, 50)
+    mfma_loop = max(Bd.arl2_profile_mfma_peak(4096, stream) for _ in range(3))
+
+    fa, fb, fc = flops(B, H, d, L)
+    passes = w.passes_per_frame
+    frame_flops = passes * (fa + fb) + fc
+    tflops = frame_flops * fps / 1e12
+    digest = source_digest("attn.hip", "arl2_device.h", "delta_chunk.h")
+    res = {
+        "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1000.0 * main_leg["wall"] / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "d": d, "L": L,
+                   "launch": "HIP graph replay" if args.graph else "eager",
+                   "passes_per_frame": f"{w.noisy_passes} query-only + 1 clean",
+                   "distinct_frames_cycled": NUM_DISTINCT_FRAMES},
+        "tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "gflop_per_frame": round(frame_flops / 1e9, 3),
+        "event_ms_per_step": round(main_leg["event_ms"] / args.steps, 5),
+        "frame_latency": main_leg["frame_latency"],
+        "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "kernels_us_warm": {k: round(v, 2) for k, v in main_leg["kernels_us_warm"].items()},
+        "kernels_timing": "kernels_us: in sequence, HIP events from the kernels' own start and "
+                          f"end (repeat 1, {args.profile_steps} frames); kernels_us_warm: each "
+                          f"idempotent launch {args.profile_repeat} times back to back between "
+                          "two event markers",
+    }
+    if d == 128 and w.dtype == SI.BF16 and args.access == "frame" and "attn_partial" in kern_us:
+        att_us = kern_us["attn_partial"]
+        att_tflops = fa / (att_us * 1e-6) / 1e12
+        traffic = measured_traffic("attn_partial", args.workload, digest)
+        alg_bytes = method_bytes(B, H, d, L)["attn_partial"]["method"]
+        res["roofline"] = {
+            "bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic, "kernel": "attn_partial (query-only pass, first launch)",
+            "per_launch": f"4*B*H*L^2*d = {fa / 1e9:.3f} GFLOP (one pass, B={B} H={H} L={L} "
+                          f"d={d})",
+            "avg_launch_us": round(att_us, 2),
+            "timing": "in sequence: HIP events from the kernel's own start and end",
+            "warm_repeat_us": round(main_leg["kernels_us_warm"].get("attn_partial", 0.0), 2),
+            "frac_of_measured_mfma_loop": round(att_tflops / mfma_loop, 4),
+            "traffic_ratio": round(traffic / alg_bytes, 3) if traffic else None,
+            "algorithmic_bytes": alg_bytes}
+        if "attn_delta" in kern_us:
+            dt = kern_us["attn_delta"] - att_us
+            res["delta_update"] = {
+                "bound": "mfma", "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "per_clean_pass": f"8*B*H*L*d^2 = {fc / 1e9:.3f} GFLOP algorithmic; the split-bf16 "
+                                  f"products execute {2 * fc / 1e9:.3f} GFLOP",
+                "added_us": round(dt, 2),
+                "achieved": round(fc / (dt * 1e-6) / 1e12, 2) if dt > 0 else None,
+                "frac": round(fc / (dt * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4) if dt > 0 else None,
+                "executed_tflops": round(2 * fc / (dt * 1e-6) / 1e12, 2) if dt > 0 else None,
+                "timing": "in sequence: the clean pass's first launch (attention + delta chunks) "
+                          "minus the query-only pass's (attention alone)"}
+        epi = {}
+        mb = method_bytes(B, H, d, L)
+        for name in ("combine", "combine_apply"):
+            if name in kern_us:
+                nbytes = mb[name]["method"]
+                gbs = nbytes / (kern_us[name] * 1e-6) / 1e9
+                epi[name] = {"bound": "hbm", "bytes": int(nbytes),
+                             "scratch_bytes": int(mb[name]["scratch"]),
+                             "avg_launch_us": round(kern_us[name], 2), "achieved": round(gbs, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        res["epilogues"] = epi
+    res["mfma_loop_peak_tflops"] = round(mfma_loop, 1)
+    if extra is not None:
+        res["frame_step_1p1"] = extra
+    res["gate_projections"] = gate_leg
+    if not args.no_cpu_baseline:
+        host = []
+        for fr in main_leg["frames"][:2]:
+            host.append([{"q": p.q.float().cpu().numpy(), "k": p.k.float().cpu().numpy(),
+                          "v": p.v.float().cpu().numpy(), "alpha": p.alpha.cpu().numpy(),
+                          "beta": p.beta.cpu().numpy(), "update": p.update} for p in fr])
+        W = SI.make_weights(w)
+        res["cpu_baseline"] = cpu_baseline(host, W, w, access=args.access)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def time_schedule(w, dev, stream, steps, warmup, access, graph=False, profile_steps=100,
+                  profile_repeat=10):
+    """Draw NUM_DISTINCT_FRAMES frames of workload w on the GPU, then: warm
+    up, time `steps` frames (cycled) between two synchronizations, time 200
+    frames one by one with HIP events, and take per-kernel times in sequence
+    (repeat 1) and, if profile_repeat > 1, warm (repeated back to back)."""
+    import torch
+
+    import synth_inputs as SI
+    from hybrid_softmax_gated_amd import binding as Bd
+    from hybrid_softmax_gated_amd.layer import ARL2Layer
+
+    B, H, d, L = w.B, w.H, w.d, w.L
+    Wd = torch.from_numpy(SI.make_weights(w)).to(dev).to(torch.bfloat16)
+    frames, cur = [], []
+    for p in SI.iter_passes_device(w, dev, frames=NUM_DISTINCT_FRAMES):
         cur.append(p)
         if p.update:
             frames.append(cur)
             cur = []
     layer = ARL2Layer(B, H, d, L, Bd.ARL2_BF16)
     out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step(i, s=stream):
         for p in frames[i % len(frames)]:
-            if args.access == "token":
+            if access == "token":
                 layer.forward_token_level(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, s)
             else:
-                layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, s,
-                              gate=w.gate)
+                layer.forward(p.q, p.k, p.v, Wd, p.alpha, p.beta, out, p.update, s, gate=w.gate)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
-    graph = None
-    if args.graph:
+    g = None
+    if graph:
         # The cycle of distinct frames as one HIP graph, replayed steps / cycle times.
-        if args.steps % len(frames):
+        if steps % len(frames):
             print(f"bench.py: --graph needs --steps to be a multiple of {len(frames)}",
                   file=sys.stderr)
-            return 2
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+            return None
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             cap = torch.cuda.current_stream()
             for i in range(len(frames)):
                 step(i, cap)
         torch.cuda.synchronize()
-        graph.replay()          # one untimed replay
+        g.replay()          # one untimed replay
         torch.cuda.synchronize()
 
     # ---- timed region (single process: the barrier is the synchronize)
@@ -509,17 +641,16 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    if graph is not None:
-        for _ in range(args.steps // len(frames)):
-            graph.replay()
+    if g is not None:
+        for _ in range(steps // len(frames)):
+            g.replay()
     else:
-        for i in range(args.steps):
+        for i in range(steps):
             step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1)
-    fps = args.steps / wall
+    event_ms = ev0.elapsed_time(ev1)
     assert torch.isfinite(layer.S).all(), "state went non-finite during the benchmark"
 
     # ---- per-frame latency: HIP events around each frame (eager), after 10
@@ -540,70 +671,20 @@ def main() -> int:
                      "frames": len(per_frame), "warmup": 10,
                      "timing": "HIP events around each frame's passes, eager launches"}
 
-    # ---- per-kernel durations with HIP events on the launch stream
-    Bd.arl2_profile_reset()
-    Bd.arl2_profile_enable(True, args.profile_repeat)
-    for i in range(args.profile_steps):
-        step(i)
-    torch.cuda.synchronize()
-    rep = Bd.arl2_profile_report()
-    Bd.arl2_profile_enable(False)
-    kern_us = {k: 1000.0 * ms / n for k, (n, ms) in rep.items() if n}
+    def kernel_times(repeat):
+        Bd.arl2_profile_reset()
+        Bd.arl2_profile_enable(True, repeat)
+        for i in range(profile_steps):
+            step(i)
+        torch.cuda.synchronize()
+        rep = Bd.arl2_profile_report()
+        Bd.arl2_profile_enable(False)
+        return {k: 1000.0 * ms / n for k, (n, ms) in rep.items() if n}
 
-    gate_leg = gate_projection_leg(w, dev, stream, 20, 50)
-    mfma_loop = max(Bd.arl2_profile_mfma_peak(4096, stream) for _ in range(3))
-    epilogues = {}
-    if d == 128 and w.dtype == SI.BF16 and args.access == "frame":
-        for name, nbytes in epilogue_bytes(B, H, d, L).items():
-            if name in kern_us:
-                gbs = nbytes / (kern_us[name] * 1e-6) / 1e9
-                epilogues[name] = {"bound": "hbm", "bytes": int(nbytes), "avg_launch_us": round(kern_us[name], 2),
-                                   "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                   "frac": round(gbs / PEAK_HBM_GBS, 4)}
-
-    fa, fb, fc = flops(B, H, d, L)
-    passes = w.passes_per_frame
-    frame_flops = passes * (fa + fb) + fc
-    tflops = frame_flops * fps / 1e12
-    att_s = kern_us["attn_partial"] * 1e-6
-    att_tflops = fa / att_s / 1e12
-    digest = source_digest("attn.hip", "arl2_device.h")
-    roofline = {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic("attn_partial", args.workload, digest),
-                "kernel": "attn_partial",
-                "per_launch": f"4*B*H*L^2*d = {fa / 1e9:.3f} GFLOP (one pass, B={B} H={H} L={L} d={d})",
-                "avg_launch_us": round(kern_us["attn_partial"], 2),
-                "frac_of_measured_mfma_loop": round(att_tflops / mfma_loop, 4)}
-
-    res = {
-        "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1000.0 * wall / args.steps, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "d": d, "L": L,
-                   "launch": "HIP graph replay" if graph is not None else "eager",
-                   "passes_per_frame": f"{w.noisy_passes} query-only + 1 clean",
-                   "distinct_frames_cycled": NUM_DISTINCT_FRAMES},
-        "tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "gflop_per_frame": round(frame_flops / 1e9, 3),
-        "event_ms_per_step": round(ev_ms / args.steps, 5),
-        "frame_latency": frame_latency,
-        "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
-        "roofline": roofline,
-        "mfma_loop_peak_tflops": round(mfma_loop, 1),
-        "epilogues": epilogues,
-        "gate_projections": gate_leg,
-    }
-    if not args.no_cpu_baseline:
-        host = []
-        for fr in frames[:2]:
-            host.append([{"q": p.q.float().cpu().numpy(), "k": p.k.float().cpu().numpy(),
-                          "v": p.v.float().cpu().numpy(), "alpha": p.alpha.cpu().numpy(),
-                          "beta": p.beta.cpu().numpy(), "update": p.update} for p in fr])
-        res["cpu_baseline"] = cpu_baseline(host, W, w, access=args.access)
-    print(json.dumps(res), flush=True)
-    return 0
+    kern_us = kernel_times(1)
+    kern_warm = kernel_times(profile_repeat) if profile_repeat > 1 else {}
+    return {"fps": steps / wall, "wall": wall, "event_ms": event_ms, "frames": frames,
+            "frame_latency": frame_latency, "kernels_us": kern_us, "kernels_us_warm": kern_warm}
 
 
 if __name__ == "__main__":

@@ -3,13 +3,16 @@
 //
 // Pass structure ("Technical Summary: Attend Locally, Remember Linearly
 // (ARL2)", section 2.2): every pass computes out = O_intra + Q' S_{N-1};
-// only the clean pass (update_flag = 1) then updates S. In stream order:
-//   1. intra-frame attention partials over key ranges   -> workspace
-//   2. merge partials + Q' = L2norm(q W_q), O_inter = Q'S -> out
-//   3. (clean pass) per-chunk dS_c = K'^T diag(beta)(V' - K'S) -> workspace
-//   4. (clean pass) S = alpha S + sum_c dS_c
-// Step 2 reads S before step 3 and 4 run, so every token of the frame reads
-// the pre-update state.
+// only the clean pass (update_flag = 1) then updates S. On the bf16 d = 128
+// path a pass is two launches, in stream order:
+//   1. intra-frame attention partials over key ranges       -> workspace
+//      S16 := bf16(S), the copy the inter-frame read uses    -> workspace
+//      (clean pass) per-chunk dS_c = K'^T diag(beta)(V' - K'S) -> workspace
+//   2. merge partials + Q' = L2norm(q W_q), O_inter = Q' S16  -> out
+//      (clean pass) S = alpha S + sum_c dS_c, in place
+// Launch 1 only reads S; in launch 2 the read goes through S16, written in
+// launch 1, so every token of the frame reads the pre-update state while S
+// itself is updated.
 #include "arl2.h"
 
 #include <hip/hip_runtime.h>
@@ -23,6 +26,10 @@
 #include <vector>
 
 #include "arl2_kernels.h"
+
+namespace arl2 {
+thread_local LaunchTiming *g_launch_timing = nullptr;
+}  // namespace arl2
 
 namespace {
 
@@ -82,7 +89,7 @@ struct FramePlan {
   bool mfma = false;
   arl2::AttnPlan ap;
   int chunk = 0, nchunk = 0;  // tokens per delta chunk, chunks per frame
-  size_t off_o = 0, off_ml = 0, off_ds = 0, total = 0;
+  size_t off_o = 0, off_ml = 0, off_ds = 0, off_s16 = 0, total = 0;
 };
 
 FramePlan plan_frame(int64_t B, int64_t H, int64_t d, int64_t L, int32_t dtype) {
@@ -103,10 +110,13 @@ FramePlan plan_frame(int64_t B, int64_t H, int64_t d, int64_t L, int32_t dtype) 
     fp.nchunk = (int)((L + arl2::kGenChunk - 1) / arl2::kGenChunk);
   }
   const size_t ds_bytes = (size_t)B * H * fp.nchunk * d * d * sizeof(float);
+  // The bf16 copy of the state that the inter-frame read uses (MFMA path).
+  const size_t s16_bytes = fp.mfma ? (size_t)B * H * d * d * 2 : 0;
   fp.off_o = 0;
   fp.off_ml = align256(o_bytes);
   fp.off_ds = fp.off_ml + align256(ml_bytes);
-  fp.total = fp.off_ds + align256(ds_bytes);
+  fp.off_s16 = fp.off_ds + align256(ds_bytes);
+  fp.total = fp.off_s16 + align256(s16_bytes);
   return fp;
 }
 
@@ -193,10 +203,13 @@ Profiler &profiler() {
   return p;
 }
 
-// Launch through `fn`, bracketed by timing events when profiling is on. A
-// kernel that only reads its inputs and overwrites its outputs (idempotent)
-// is launched `repeat` times back to back between the two events, so that
-// the events' own overhead is spread over the launches.
+// Launch through `fn`, timed when profiling is on. With repeat = 1, or for
+// a kernel that updates memory it reads (not idempotent), the two events are
+// taken from the kernels' own start and end (arl2::launch with a timing
+// region open), so the time is that of the launch in its place in the
+// sequence. With repeat > 1 an idempotent launch is repeated back to back
+// between two event markers, which spreads the markers' own overhead over
+// the repeats (warm caches, no gaps to the neighbouring launches).
 template <class F>
 hipError_t timed(const char *name, hipStream_t s, F fn, bool idempotent = true) {
   Profiler &p = profiler();
@@ -210,10 +223,19 @@ hipError_t timed(const char *name, hipStream_t s, F fn, bool idempotent = true) 
   if (e != hipSuccess) return e;
   if ((e = p.event(&b)) != hipSuccess) return e;
   const int count = idempotent ? p.repeat : 1;
-  if ((e = hipEventRecord(a, s)) != hipSuccess) return e;
-  for (int i = 0; i < count; ++i)
-    if ((e = fn()) != hipSuccess) return e;
-  if ((e = hipEventRecord(b, s)) != hipSuccess) return e;
+  if (count == 1) {
+    arl2::LaunchTiming lt{a, b, false};
+    arl2::g_launch_timing = &lt;
+    e = fn();
+    arl2::g_launch_timing = nullptr;
+    if (e != hipSuccess) return e;
+    if (!lt.started) return hipErrorInvalidValue;  // nothing was launched
+  } else {
+    if ((e = hipEventRecord(a, s)) != hipSuccess) return e;
+    for (int i = 0; i < count; ++i)
+      if ((e = fn()) != hipSuccess) return e;
+    if ((e = hipEventRecord(b, s)) != hipSuccess) return e;
+  }
   p.pending.push_back({count, p.id(name), a, b});
   return hipSuccess;
 }
@@ -433,6 +455,7 @@ arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, con
   float *ws_o = (float *)(ws + fp.off_o);
   float *ws_ml = (float *)(ws + fp.off_ml);
   float *ws_ds = (float *)(ws + fp.off_ds);
+  void *ws_s16 = ws + fp.off_s16;
   const char *wbase = (const char *)Wphi;
   const void *Wq = wbase;
   const void *Wk = wbase + (size_t)H * d * d * es;
@@ -443,14 +466,20 @@ arl2_status frame_forward_impl(const char *fn, const void *q, const void *k, con
   hipError_t e;
   if (fp.mfma) {
     const arl2::AttnArgs aa{q, k, v, iB, iH, iL, iL, fp.ap, ws_o, ws_ml};
-    const arl2::CombineArgs ca{ws_o, ws_ml, q, Wq, S, iB, iH, iL, fp.ap, out};
+    const arl2::CombineArgs ca{ws_o, ws_ml, q, Wq, ws_s16, iB, iH, iL, fp.ap, out};
     const arl2::DeltaArgs da{k, v, Wk, Wv, S, beta, iB, iH, iL, fp.chunk, fp.nchunk, ws_ds};
-    if ((e = timed("attn_partial", s, [&] { return arl2::launch_attn_partial_bf16(aa, s); })))
-      return hip_status(e, fn);
-    if ((e = timed(update_flag ? "combine_delta" : "combine", s, [&] {
-           return arl2::launch_tail_bf16(ca, update_flag ? &da : nullptr, s);
+    const arl2::ApplyArgs ap{S, alpha, gate == ARL2_GATE_ELEMENTWISE, ws_ds, iB, iH, fp.nchunk};
+    const int64_t nstate = B * H * d * d;
+    if ((e = timed(update_flag ? "attn_delta" : "attn_partial", s, [&] {
+           return arl2::launch_pass_head_bf16(aa, update_flag ? &da : nullptr, S, ws_s16, nstate,
+                                              s);
          })))
       return hip_status(e, fn);
+    if ((e = timed(update_flag ? "combine_apply" : "combine", s, [&] {
+           return arl2::launch_tail_bf16(ca, update_flag ? &ap : nullptr, s);
+         }, /*idempotent=*/update_flag == 0)))
+      return hip_status(e, fn);
+    return ok();
   } else {
     if ((e = timed("generic_attention", s, [&] {
            return arl2::launch_generic_attention(dt, id, q, k, v, iB, iH, iL, iL, ws_o, s);

@@ -2,11 +2,35 @@
 // Not installed; the public interface is include/arl2.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace arl2 {
+
+// ---------------------------------------------------------------- launches
+// Kernel timing (arl2_profile_enable): while a caller's timing region is
+// open on this thread, every launch records the region's `start` event at
+// the first kernel's start and its `stop` event at each kernel's end
+// (hipExtLaunchKernel events, taken from the kernels' own dispatch), so the
+// pair brackets the kernels themselves, with no marker between them.
+struct LaunchTiming {
+  hipEvent_t start, stop;
+  bool started;
+};
+extern thread_local LaunchTiming *g_launch_timing;
+
+template <class F, class... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, Args... args) {
+  if (LaunchTiming *t = g_launch_timing) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, t->started ? nullptr : t->start, t->stop,
+                          0, args...);
+    t->started = true;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
+}
 
 // ---------------------------------------------------------------- plans
 // How one attention call is cut into workgroups: query blocks of 128 rows
@@ -49,9 +73,9 @@ hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s);
 struct CombineArgs {
   const void *ws_o;
   const float *ws_ml;
-  const void *q;   // [B][L][H][128]
-  const void *Wq;  // [H][128][128], or null
-  const float *S;  // [B][H][128][128] (read when Wq is set)
+  const void *q;    // [B][L][H][128]
+  const void *Wq;   // [H][128][128], or null
+  const void *S16;  // [B][H][128][128] bf16 copy of the state (read when Wq is set)
   int B, H, L;
   AttnPlan plan;
   void *out;  // [B][L][H][128] bf16
@@ -75,9 +99,26 @@ struct DeltaArgs {
 // 128 (fewer chunk contributions to write and sum).
 int delta_chunk_tokens(int64_t B, int64_t H, int64_t L);
 
-// One launch for the combine and, when `d` is not null, the delta chunks:
-// both only read S, so they run side by side.
-hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_t s);
+// The first launch of a pass: the attention partials, the delta chunks
+// when `d` is not null (clean pass), and S16 := bf16(S) for `state_values`
+// values (a multiple of 2048) when S is not null. All of them only read S.
+hipError_t launch_pass_head_bf16(const AttnArgs &a, const DeltaArgs *d, const float *S, void *S16,
+                                 int64_t state_values, hipStream_t s);
+
+// S := gate(S) + sum over chunks c (in order) of ws_dS[b][h][c], as items of
+// the second launch of a clean pass (gate as in launch_delta_apply).
+struct ApplyArgs {
+  float *S;
+  const float *alpha;
+  bool elementwise;
+  const float *ws_dS;
+  int B, H, nchunk;
+};
+
+// The second launch of a pass: the combine and, when `ap` is not null, the
+// state update from the chunk contributions. The combine reads only the
+// bf16 copy of the state, so the in-place update can share the launch.
+hipError_t launch_tail_bf16(const CombineArgs &c, const ApplyArgs *ap, hipStream_t s);
 
 // ---------------------------------------------------------------- shared
 // S[b][h] := gate(S[b][h]) + sum over chunks c (in order) of ws_dS[b][h][c],

@@ -1,18 +1,21 @@
-// Intra-frame softmax attention (bf16, d = 128) on the gfx950 matrix cores,
-// and the combine kernel that merges its key-range partials with the
-// inter-frame read O_inter = Q' S and writes the layer output.
+// The first launch of a pass (bf16 io, d = 128): intra-frame softmax
+// attention on the gfx950 matrix cores, written as partial results per key
+// range; on a clean pass also the chunk contributions of the gated delta
+// state update (delta_chunk.h); and a bf16 copy of the state for the
+// inter-frame read of the second launch.
 //
 // Method: "Technical Summary: Attend Locally, Remember Linearly (ARL2)",
 // section 2.1 — the intra-frame branch keeps full bidirectional softmax
 // attention inside the frame; the inter-frame branch reads the fixed-size
-// state with feature-mapped, L2-normalised queries; every token of the frame
-// reads the same pre-update state (section 2.2, frame-level access).
+// state with feature-mapped, L2-normalised queries; section 2.2 — every token
+// of the frame reads the same pre-update state, and only the clean pass
+// writes it.
 //
 // Data layout in HBM: q, k, v, out are token-major [B][L][H][128] bf16, so a
 // head's row of 128 values is 256 contiguous bytes and consecutive tokens of
 // one head are H*256 bytes apart.
 //
-// Attention kernel (one workgroup = 4 wavefronts = 128 queries of one head,
+// Attention items (one workgroup = 4 wavefronts = 128 queries of one head,
 // one contiguous key range; two workgroups per compute unit):
 //  * each wavefront keeps its 32 queries in registers as MFMA B operands and
 //    computes the transposed score tile S^T = K Q^T (keys on rows), so every
@@ -30,13 +33,11 @@
 //  * per key range it writes O/l in bf16, in the accumulators' register
 //    order (16-byte coalesced stores), and the row max (log2 domain) and row
 //    sum in fp32.
-//
-// Combine kernel (one workgroup = 128 queries of one head): the inter-frame
-// read (q W_q, L2 norms, Q' S on the matrix cores, with W_q and bf16(S) in
-// LDS), the merge of the key ranges in fp32, the sum of the two branches,
-// and the bf16 output rows, transposed through LDS into 256-byte stores.
+// Update chunks and state-copy items take the workgroup ids after the
+// attention items; all three only read the state, so they share the launch.
 #include "arl2_device.h"
 #include "arl2_kernels.h"
+#include "delta_chunk.h"
 
 #include <math.h>
 
@@ -67,16 +68,11 @@ __device__ __forceinline__ int item_of(int bid, int per_xcd) {
   return (bid & 7) * per_xcd + (bid >> 3);
 }
 
-__global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
-  // Double-buffered K and V tiles, each its own array so that the compiler
-  // sees the copies into one buffer and the reads of the other as disjoint.
-  __shared__ __attribute__((aligned(1024))) char Ks0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Ks1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Vs0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char Vs1[TILE_BYTES];
-
-  const int item = item_of(blockIdx.x, p.per_xcd);
-  if (item >= p.nitems) return;
+// One attention item. Ks0/Ks1/Vs0/Vs1: double-buffered K and V tiles, each
+// its own LDS array so that the compiler sees the copies into one buffer and
+// the reads of the other as disjoint.
+__device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *Ks0, char *Ks1,
+                                          char *Vs0, char *Vs1) {
   const int qblk = item % p.nqblk;
   int rest = item / p.nqblk;
   const int split = rest % p.nsplit;
@@ -270,6 +266,58 @@ __global__ __launch_bounds__(256, 2) void attn_partial_kernel(AttnKParams p) {
   }
 }
 
+// S16 := bf16(S) (round to nearest even) for 2048 state values per item.
+__device__ __forceinline__ void state_copy_body(const float *S, bf16 *S16, int item) {
+  const int64_t i0 = (int64_t)item * 2048 + threadIdx.x * 8;
+  const f32x4 a = *(const f32x4 *)(S + i0);
+  const f32x4 c = *(const f32x4 *)(S + i0 + 4);
+  bf16x8 t;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    t[e] = (bf16)a[e];
+    t[4 + e] = (bf16)c[e];
+  }
+  *(bf16x8 *)(S16 + i0) = t;
+}
+
+struct PassKParams {
+  AttnKParams a;
+  DeltaKParams d;
+  const float *S;   // state to copy (null: no copy items)
+  bf16 *S16;
+  int attn_blocks;  // workgroups of attention items (8 * per_xcd)
+  int delta_blocks; // workgroups of update chunks (8 * per_xcd_d)
+  int per_xcd_d;
+  int copy_items;
+};
+
+// Workgroups [0, attn_blocks): attention; then the update chunks (dealt to
+// XCDs in contiguous runs, so one head's chunks share an L2 for its weights
+// and state); then the state copy.
+template <int NT>
+__global__ __launch_bounds__(256, 2) void pass_head_kernel(PassKParams P) {
+  __shared__ __attribute__((aligned(1024))) char Ks0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ks1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Vs0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Vs1[TILE_BYTES];
+  __shared__ float betas[32 * 4];
+  int bid = blockIdx.x;
+  if (bid < P.attn_blocks) {
+    const int item = item_of(bid, P.a.per_xcd);
+    if (item < P.a.nitems) attn_body(P.a, item, Ks0, Ks1, Vs0, Vs1);
+    return;
+  }
+  bid -= P.attn_blocks;
+  if (bid < P.delta_blocks) {
+    const int item = item_of(bid, P.per_xcd_d);
+    if (item < P.d.nitems)
+      delta_body<NT>(P.d, item, SplitTile{Ks0, Ks1}, SplitTile{Vs0, Vs1}, betas);
+    return;
+  }
+  bid -= P.delta_blocks;
+  if (bid < P.copy_items) state_copy_body(P.S, P.S16, bid);
+}
+
 }  // namespace
 
 AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
@@ -291,7 +339,7 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
   return pl;
 }
 
-hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s) {
+static AttnKParams attn_params(const AttnArgs &a) {
   AttnKParams p;
   p.q = (const bf16 *)a.q;
   p.k = (const bf16 *)a.k;
@@ -308,8 +356,47 @@ hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s) {
   p.scale = kLog2e / sqrtf((float)D);
   p.nitems = a.B * a.H * a.plan.nsplit * a.plan.nqblk;
   p.per_xcd = (p.nitems + 7) / 8;
-  hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)(8 * p.per_xcd)), dim3(256), 0, s, p);
+  return p;
+}
+
+hipError_t launch_pass_head_bf16(const AttnArgs &a, const DeltaArgs *d, const float *S, void *S16,
+                                 int64_t state_values, hipStream_t s) {
+  if (d && d->chunk != 96 && d->chunk != 128) return hipErrorInvalidValue;
+  if (S && state_values % 2048 != 0) return hipErrorInvalidValue;
+  PassKParams P;
+  P.a = attn_params(a);
+  P.attn_blocks = 8 * P.a.per_xcd;
+  P.d = DeltaKParams{};
+  P.delta_blocks = 0;
+  P.per_xcd_d = 0;
+  if (d) {
+    P.d.k = (const bf16 *)d->k;
+    P.d.v = (const bf16 *)d->v;
+    P.d.Wk = (const bf16 *)d->Wk;
+    P.d.Wv = (const bf16 *)d->Wv;
+    P.d.S = d->S;
+    P.d.beta = d->beta;
+    P.d.H = d->H;
+    P.d.L = d->L;
+    P.d.nchunk = d->nchunk;
+    P.d.nitems = d->B * d->H * d->nchunk;
+    P.d.ws_dS = d->ws_dS;
+    P.per_xcd_d = (P.d.nitems + 7) / 8;
+    P.delta_blocks = 8 * P.per_xcd_d;
+  }
+  P.S = S;
+  P.S16 = (bf16 *)S16;
+  P.copy_items = S ? (int)(state_values / 2048) : 0;
+  const unsigned blocks = (unsigned)(P.attn_blocks + P.delta_blocks + P.copy_items);
+  if (d && d->chunk == 96)
+    launch(pass_head_kernel<3>, dim3(blocks), dim3(256), 0, s, P);
+  else
+    launch(pass_head_kernel<4>, dim3(blocks), dim3(256), 0, s, P);
   return hipGetLastError();
+}
+
+hipError_t launch_attn_partial_bf16(const AttnArgs &a, hipStream_t s) {
+  return launch_pass_head_bf16(a, nullptr, nullptr, nullptr, 0, s);
 }
 
 }  // namespace arl2

@@ -1,44 +1,16 @@
-// The work after the attention kernel in one pass: the combine (merge of
-// the attention partials, the inter-frame read and the output), and on the
-// clean pass the gated delta state update. Both only read the state, so
-// they share one launch; a last kernel applies the update in place.
-//
-// Gated delta state update of the inter-frame branch (bf16 io, d = 128):
+// The second launch of a pass: the combine (merge of the attention
+// partials, the inter-frame read and the output) and, on the clean pass, the
+// in-place state update from the chunk contributions that the first launch
+// computed (delta_chunk.h). The combine reads only the bf16 copy of the
+// pre-update state that the first launch made, so the update of S shares
+// the launch.
 //
 // Method: "Technical Summary: Attend Locally, Remember Linearly (ARL2)",
-// section 2.1 (state update) and section 2.2 (the state is written once per
-// frame, after the clean pass, from the pre-update state):
-//   K' = L2norm(k W_k), V' = v W_v, R = V' - K' S_{N-1},
-//   S_N = alpha S_{N-1} + K'^T diag(beta) R.
-//
-// Work split: one workgroup per chunk of 32*NT tokens of one (stream, head)
-// computes that chunk's contribution dS_c = K'_c^T diag(beta_c) R_c into the
-// workspace; delta_apply_kernel then applies S = alpha S + sum_c dS_c in a
-// fixed chunk order (deterministic, no atomics). Every workgroup of the
-// first launch reads the same pre-update S, so the in-place write is safe.
-//
-// Precision: the feature maps use bf16 operands (the inputs are bf16) with
-// fp32 accumulation, which is exact per product. The two products that
-// involve the fp32 state or the fp32 K' — K'S and K'^T (beta R) — use the
-// split-bf16 scheme (x = hi + lo, three MFMAs hi*hi + hi*lo + lo*hi; Henry,
-// Tang and Heinecke, ARITH 2019), about 2^-16 relative per product, because
-// plain bf16 operands lose about 2^-9 per frame on the state.
-//
-// Within a workgroup (4 wavefronts; wavefront w owns state columns
-// d_v in [32w, 32w + 32)):
-//  (0) W_k and W_v are copied into LDS as swizzled 128x128 tiles; each wave
-//      keeps -S[:, its columns] in registers as split-bf16 MFMA operands;
-//  (1) wave t < NT computes (k W_k)^T for token tile t (lanes = tokens,
-//      registers = d_k), the L2 norms in registers, and writes K' (split
-//      bf16, rows = tokens) over the weight tiles;
-//  (2) every wave forms R = v W_v - K'S for all tokens of the chunk and its
-//      columns (rows = tokens), scales by beta and keeps the result as
-//      split-bf16 operands in registers (the accumulator rows line up with
-//      the k order of the next product);
-//  (3) every wave contracts over the tokens: dS_c[:, its columns] =
-//      K'^T (beta R), with K'^T read transposed from LDS.
-// No product is computed twice; LDS holds 64 KB, so two workgroups share a
-// compute unit.
+// section 2.1 (out = O_intra + Q' S_{N-1}; S_N = alpha S_{N-1} +
+// K'^T diag(beta)(V' - K' S_{N-1})) and section 2.2 (every token of the frame
+// reads the pre-update state; the state is written once per frame, after
+// the clean pass). The chunk contributions are summed in a fixed chunk order
+// (deterministic, no atomics).
 #include "arl2_device.h"
 #include "arl2_kernels.h"
 
@@ -54,7 +26,7 @@ struct CombineKParams {
   const char *ws_o;
   const float *ws_ml;
   const bf16 *q, *Wq;  // Wq null: no inter-frame read (plain attention)
-  const float *S;
+  const bf16 *S16;     // bf16 copy of the pre-update state
   int H, L, nqblk, nsplit, nitems;
   bf16 *out;
   const float *o_inter;  // [B][L][H][128] fp32, added when set (and Wq null)
@@ -65,9 +37,9 @@ struct CombineKParams {
 // m_s. Lanes own queries and registers own d_v, as in the attention
 // kernel's accumulators, so the partials are read in the order they were
 // written and O_inter comes out of the MFMAs in the same layout.
-// Every load is issued before any arithmetic: the state rows (converted to
-// bf16 into LDS first, which frees their registers), W_q, the queries, the
-// merge weights and the first kPre key ranges' partials. The merge runs
+// Every load is issued before any arithmetic: bf16(S) and W_q (copied into
+// LDS), the queries, the merge weights and the first kPre key ranges'
+// partials. The merge runs
 // first and the inter-frame read's last product accumulates onto it.
 // Wt: 32 KB of LDS for W_q[h], then the output rows; St: 32 KB for bf16(S).
 __device__ __forceinline__ void combine_body(const CombineKParams p, int item, char *Wt,
@@ -81,23 +53,18 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
   const int qrow = qblk * kQBlock + wave * 32 + l32;
   const bool inter = p.Wq != nullptr;
 
-  // State rows (fp32) and W_q[h] (straight into LDS, swizzled).
-  f32x4 sx[8][2];
+  // bf16(S)[h] and W_q[h], straight into LDS (swizzled).
   bf16x8 qop[8];
   if (inter) {
-    const float *Sh = p.S + ((int64_t)b * p.H + h) * D * D;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 4) + 16 * i, u = tid & 15;
-      sx[i][0] = *(const f32x4 *)(Sh + row * D + 8 * u);
-      sx[i][1] = *(const f32x4 *)(Sh + row * D + 8 * u + 4);
-    }
+    const bf16 *Sh = p.S16 + ((int64_t)b * p.H + h) * D * D;
     const bf16 *W = p.Wq + (int64_t)h * D * D;
     const int r4 = lane >> 4, pos = lane & 15;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int cc = 8 * wave + i, row = 4 * cc + r4;
-      global_to_lds16(W + row * D + 8 * (pos ^ tile_swz(row & 15)), Wt + cc * 1024);
+      const int off = row * D + 8 * (pos ^ tile_swz(row & 15));
+      global_to_lds16(Sh + off, St + cc * 1024);
+      global_to_lds16(W + off, Wt + cc * 1024);
     }
     // The wave's 32 queries as B operands: lane l holds query l%32,
     // features 16c + 8*(l/32) .. +7 (zeros past the frame).
@@ -134,20 +101,6 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
       for (int u = 0; u < 8; ++u)
         pr[s][u] = *(const bf16x8 *)(src + s * kPartialOBytes + u * 64 * 16);
     }
-
-  if (inter) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 4) + 16 * i, u = tid & 15;
-      bf16x8 t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t[e] = (bf16)sx[i][0][e];
-        t[4 + e] = (bf16)sx[i][1][e];
-      }
-      *(bf16x8 *)(St + tile_off(row, u)) = t;
-    }
-  }
 
   float M = -INFINITY;
 #pragma unroll
@@ -264,243 +217,65 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
   }
 }
 
-struct DeltaKParams {
-  const bf16 *k, *v, *Wk, *Wv;
-  const float *S, *beta;
-  int H, L, nchunk, nitems;
-  float *ws_dS;
+struct ApplyKParams {
+  float *S;
+  const float *alpha;
+  int arow4;  // 0: one gate per (stream, head); else 4-value groups per d_k row
+  const float *ws;
+  int nchunk, nitems;
 };
 
-// One chunk of 32*NT tokens (item = (stream, head, chunk), chunk fastest).
-// bufA holds W_k, then K' (hi); bufB W_v, then K' (lo); 32 KB each.
-template <int NT>
-__device__ __forceinline__ void delta_body(const DeltaKParams p, int item, char *bufA, char *bufB,
-                                           float *betas) {
-  static_assert(NT >= 1 && NT <= 4, "token tiles per chunk");
-  constexpr int T = 32 * NT;
-  const int chunk = item % p.nchunk;
-  const int rest = item / p.nchunk;
-  const int h = rest % p.H, b = rest / p.H;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-  const int t0 = chunk * T;
-  const int nvalid = min(T, p.L - t0);
-  const int tokB = p.H * D * 2;  // bytes between tokens (H <= 65535)
-  const char *kbase = (const char *)(p.k + (((int64_t)b * p.L + t0) * p.H + h) * D);
-  const char *vbase = (const char *)(p.v + (((int64_t)b * p.L + t0) * p.H + h) * D);
-  // Rows at or past the chunk's last valid token read as zeros.
-  const uint32_t span = (uint32_t)nvalid * (uint32_t)tokB;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, span);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, span);
-
-  // (0) Weight tiles: wave w copies 4-row chunks 8w .. 8w+7 of each map;
-  // lane (r4 = l/16, pos = l%16) fetches unit pos ^ swizzle of its row, so
-  // the bytes land in the swizzled layout.
-  {
-    const bf16 *Wk = p.Wk + (int64_t)h * D * D;
-    const bf16 *Wv = p.Wv + (int64_t)h * D * D;
-    const int r4 = lane >> 4, pos = lane & 15;
+// S := gate(S) + sum_c dS_c for 1024 state values of one (stream, head)
+// (item = (stream, head, block of 8 rows)), one thread per 4 consecutive
+// values; the chunk contributions are summed in chunk order, with up to 16
+// loads in flight per thread.
+__device__ __forceinline__ void apply_body(const ApplyKParams p, int item) {
+  constexpr int dd4 = D * D / 4;
+  const int bh = item >> 4;
+  const int e = (item & 15) * 256 + threadIdx.x;
+  const f32x4 *w = (const f32x4 *)p.ws + (int64_t)bh * p.nchunk * dd4 + e;
+  f32x4 *sp = (f32x4 *)p.S + (int64_t)bh * dd4 + e;
+  const f32x4 sv = *sp;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < p.nchunk; c0 += 16) {
+    f32x4 t[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int cc = 8 * wave + i, row = 4 * cc + r4;
-      const int off = row * D + 8 * (pos ^ tile_swz(row & 15));
-      global_to_lds16(Wk + off, bufA + cc * 1024);
-      global_to_lds16(Wv + off, bufB + cc * 1024);
-    }
+    for (int u = 0; u < 16; ++u)
+      if (c0 + u < p.nchunk) t[u] = w[(int64_t)(c0 + u) * dd4];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (c0 + u < p.nchunk) acc += t[u];
   }
-  if (tid < T)
-    betas[tid] = tid < nvalid ? p.beta[((int64_t)b * p.L + t0 + tid) * p.H + h] : 0.f;
-
-  // -S[d_k][d_v] for d_v = 32*wave + l%32 as B operands, split bf16: group g
-  // holds d_k = 16g + 8*(l/32) .. +7.
-  bf16x8 snh[8], snl[8];
-  {
-    const float *Sp = p.S + ((int64_t)b * p.H + h) * D * D + 32 * wave + l32;
+  const float a = p.arow4 ? p.alpha[(int64_t)bh * D + e / p.arow4] : p.alpha[bh];
+  f32x4 r;
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bf16 hi, lo;
-        split_bf16(-Sp[(16 * g + 8 * hl + j) * D], hi, lo);
-        snh[g][j] = hi;
-        snl[g][j] = lo;
-      }
-  }
-
-  // This wave's token tile (if any) as B operands: lane l holds token
-  // 32*wave + l%32, features 16c + 8*(l/32) .. +7.
-  bf16x8 kop[8];
-  if (wave < NT) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      kop[c] = buffer_load16(rk, (32 * wave + l32) * tokB + 32 * c + 16 * hl);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // (1) (k W_k)^T: rows d_k = 32bb + 8(i/4) + 4(l/32) + i%4, column = token.
-  f32x16 kt[4];
-  float inv = 0.f;
-  if (wave < NT) {
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) kt[bb] = zero16();
-    // Four independent chains, interleaved.
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int k0 = 16 * c + 8 * hl;
-      bf16x8 wa[4];
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) wa[bb] = tile_col_operand(bufA, k0, k0 + 4, lane, bb);
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) kt[bb] = mfma32(wa[bb], kop[c], kt[bb]);
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ss = fmaf(kt[bb][i], kt[bb][i], ss);
-    ss += swap_halves(ss);
-    inv = 1.f / fmaxf(sqrtf(ss), kL2Eps);
-  }
-  // W_v[d_in][d_v] for this wave's columns as B operands (k = d_in).
-  bf16x8 wv[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int k0 = 16 * c + 8 * hl;
-    wv[c] = tile_col_operand(bufB, k0, k0 + 4, lane, wave);
-  }
-  __syncthreads();  // every read of the weight tiles is done
-
-  // K' rows (split bf16) over the weight tiles: row = token, column = d_k.
-  if (wave < NT) {
-    const int row = 32 * wave + l32;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bf16x4 th, tl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bf16 hi, lo;
-          split_bf16(kt[bb][4 * r + e] * inv, hi, lo);
-          th[e] = hi;
-          tl[e] = lo;
-        }
-        const int off = tile_off(row, 4 * bb + r) + 8 * hl;
-        *(bf16x4 *)(bufA + off) = th;
-        *(bf16x4 *)(bufB + off) = tl;
-      }
-  }
-  __syncthreads();
-
-  // (2) R = v W_v - K'S per token tile, then beta R as split-bf16 B
-  // operands: accumulator registers 8*g2 .. 8*g2+7 hold tokens
-  // 16*g2 + swap_bits23(8*(l/32) + j) of the tile.
-  bf16x8 rh[NT][2], rl[NT][2];
-  bf16x8 va[8], vn[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) va[c] = buffer_load16(rv, l32 * tokB + 32 * c + 16 * hl);
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    if (tt + 1 < NT) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        vn[c] = buffer_load16(rv, (32 * (tt + 1) + l32) * tokB + 32 * c + 16 * hl);
-    }
-    // Two accumulation chains (v W_v + hi*hi, the two cross terms),
-    // alternating so that no MFMA waits on the one just before it.
-    f32x16 a0 = zero16(), a1 = zero16();
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int off = tile_off(32 * tt + l32, 2 * g + hl);
-      const bf16x8 ah = *(const bf16x8 *)(bufA + off);
-      const bf16x8 al = *(const bf16x8 *)(bufB + off);
-      a0 = mfma32(va[g], wv[g], a0);
-      a1 = mfma32(ah, snl[g], a1);
-      a0 = mfma32(ah, snh[g], a0);
-      a1 = mfma32(al, snh[g], a1);
-    }
-    f32x16 acc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = a0[i] + a1[i];
-#pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tok = 32 * tt + 16 * g2 + 8 * (j >> 2) + 4 * hl + (j & 3);
-        bf16 hi, lo;
-        split_bf16(acc[8 * g2 + j] * betas[tok], hi, lo);
-        rh[tt][g2][j] = hi;
-        rl[tt][g2][j] = lo;
-      }
-    if (tt + 1 < NT) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) va[c] = vn[c];
-    }
-  }
-
-  // (3) dS_c[d_k][d_v] = sum over tokens of K'[t][d_k] (beta R)[t][d_v]:
-  // A = K'^T read transposed (tokens in the same permuted order).
-  f32x16 ds[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) ds[db] = zero16();
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {
-      const int k0 = 32 * tt + 16 * g2 + 4 * hl;
-      bf16x8 ah[4], al[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        ah[db] = tile_col_operand(bufA, k0, k0 + 8, lane, db);
-        al[db] = tile_col_operand(bufB, k0, k0 + 8, lane, db);
-      }
-      // Four independent chains, interleaved.
-#pragma unroll
-      for (int db = 0; db < 4; ++db) ds[db] = mfma32(ah[db], rh[tt][g2], ds[db]);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) ds[db] = mfma32(ah[db], rl[tt][g2], ds[db]);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) ds[db] = mfma32(al[db], rh[tt][g2], ds[db]);
-    }
-
-  float *wd = p.ws_dS + (((int64_t)b * p.H + h) * p.nchunk + chunk) * D * D + 32 * wave + l32;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int dk = 32 * db + 8 * (i >> 2) + 4 * hl + (i & 3);
-      wd[dk * D] = ds[db][i];
-    }
+  for (int u = 0; u < 4; ++u) r[u] = fmaf(a, sv[u], acc[u]);
+  *sp = r;
 }
 
 struct TailKParams {
   CombineKParams c;
-  DeltaKParams d;
-  int delta_blocks;  // leading workgroups that run delta chunks (0: none)
-  int per_xcd_d, per_xcd_c;
+  ApplyKParams ap;
+  int apply_items;  // leading workgroups that apply the state update (0: none)
+  int per_xcd_c;
 };
 
-// Items of either kind are dealt so that each XCD gets a contiguous run
+// Items of the combine are dealt so that each XCD gets a contiguous run
 // (workgroups go to the 8 XCDs round-robin by linear id): the query blocks
-// or chunks of one head share that XCD's L2 for the head's weights and
-// state. Delta chunks take the first workgroup ids, so they start first.
+// of one head share that XCD's L2 for the head's weights and state. The
+// short update items take the first workgroup ids.
 __device__ __forceinline__ int xcd_item(int bid, int per_xcd) {
   return (bid & 7) * per_xcd + (bid >> 3);
 }
 
-template <int NT>
 __global__ __launch_bounds__(256, 2) void tail_kernel(TailKParams P) {
   __shared__ __attribute__((aligned(1024))) char lds0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char lds1[TILE_BYTES];
-  __shared__ float betas[32 * NT];
   const int bid = blockIdx.x;
-  if (bid < P.delta_blocks) {
-    const int item = xcd_item(bid, P.per_xcd_d);
-    if (item < P.d.nitems) delta_body<NT>(P.d, item, lds0, lds1, betas);
+  if (bid < P.apply_items) {
+    apply_body(P.ap, bid);
   } else {
-    const int item = xcd_item(bid - P.delta_blocks, P.per_xcd_c);
+    const int item = xcd_item(bid - P.apply_items, P.per_xcd_c);
     if (item < P.c.nitems) combine_body(P.c, item, lds0, lds1);
   }
 }
@@ -548,14 +323,13 @@ int delta_chunk_tokens(int64_t B, int64_t H, int64_t L) {
   return items <= 512 ? 96 : 128;
 }
 
-hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_t s) {
-  if (d && d->chunk != 96 && d->chunk != 128) return hipErrorInvalidValue;
+hipError_t launch_tail_bf16(const CombineArgs &c, const ApplyArgs *ap, hipStream_t s) {
   TailKParams P;
   P.c.ws_o = (const char *)c.ws_o;
   P.c.ws_ml = c.ws_ml;
   P.c.q = (const bf16 *)c.q;
   P.c.Wq = (const bf16 *)c.Wq;
-  P.c.S = c.S;
+  P.c.S16 = (const bf16 *)c.S16;
   P.c.H = c.H;
   P.c.L = c.L;
   P.c.nqblk = c.plan.nqblk;
@@ -564,29 +338,21 @@ hipError_t launch_tail_bf16(const CombineArgs &c, const DeltaArgs *d, hipStream_
   P.c.out = (bf16 *)c.out;
   P.c.o_inter = c.Wq ? nullptr : c.o_inter;
   P.per_xcd_c = (P.c.nitems + 7) / 8;
-  P.d = DeltaKParams{};
-  P.delta_blocks = 0;
-  P.per_xcd_d = 0;
-  if (d) {
-    P.d.k = (const bf16 *)d->k;
-    P.d.v = (const bf16 *)d->v;
-    P.d.Wk = (const bf16 *)d->Wk;
-    P.d.Wv = (const bf16 *)d->Wv;
-    P.d.S = d->S;
-    P.d.beta = d->beta;
-    P.d.H = d->H;
-    P.d.L = d->L;
-    P.d.nchunk = d->nchunk;
-    P.d.nitems = d->B * d->H * d->nchunk;
-    P.d.ws_dS = d->ws_dS;
-    P.per_xcd_d = (P.d.nitems + 7) / 8;
-    P.delta_blocks = 8 * P.per_xcd_d;
+  P.ap = ApplyKParams{};
+  P.apply_items = 0;
+  if (ap) {
+    P.ap.S = ap->S;
+    P.ap.alpha = ap->alpha;
+    P.ap.arow4 = ap->elementwise ? D / 4 : 0;
+    P.ap.ws = ap->ws_dS;
+    P.ap.nchunk = ap->nchunk;
+    P.ap.nitems = ap->B * ap->H * 16;
+    // A multiple of 8, so the combine items keep their XCD runs.
+    P.apply_items = (P.ap.nitems + 7) / 8 * 8;
+    if (P.apply_items != P.ap.nitems) return hipErrorInvalidValue;
   }
-  const unsigned blocks = (unsigned)(P.delta_blocks + 8 * P.per_xcd_c);
-  if (d && d->chunk == 96)
-    hipLaunchKernelGGL(tail_kernel<3>, dim3(blocks), dim3(256), 0, s, P);
-  else
-    hipLaunchKernelGGL(tail_kernel<4>, dim3(blocks), dim3(256), 0, s, P);
+  const unsigned blocks = (unsigned)(P.apply_items + 8 * P.per_xcd_c);
+  launch(tail_kernel, dim3(blocks), dim3(256), 0, s, P);
   return hipGetLastError();
 }
 
@@ -594,7 +360,7 @@ hipError_t launch_delta_apply(float *S, const float *alpha, bool elementwise, co
                               int B, int H, int d, int nchunk, hipStream_t s) {
   const int dd4 = d * d / 4;
   dim3 grid((unsigned)((dd4 + 63) / 64), (unsigned)(B * H));
-  hipLaunchKernelGGL(delta_apply_kernel, grid, dim3(64), 0, s, S, alpha, elementwise ? d / 4 : 0,
+  launch(delta_apply_kernel, grid, dim3(64), 0, s, S, alpha, elementwise ? d / 4 : 0,
                      ws_dS, dd4, nchunk);
   return hipGetLastError();
 }
@@ -602,7 +368,7 @@ hipError_t launch_delta_apply(float *S, const float *alpha, bool elementwise, co
 hipError_t launch_fill_state(float *dst, const float *src, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   dim3 grid((unsigned)((n + 255) / 256));
-  hipLaunchKernelGGL(fill_state_kernel, grid, dim3(256), 0, s, dst, src, n);
+  launch(fill_state_kernel, grid, dim3(256), 0, s, dst, src, n);
   return hipGetLastError();
 }
 

@@ -212,22 +212,22 @@ hipError_t launch_gate_projections(const GateArgs &a, hipStream_t s) {
     GateLogitParams p{(const bf16 *)a.x, (const bf16 *)a.Wa, (const bf16 *)a.Wb, a.B, a.L, a.D,
                       a.H, g.ntt, g.nnt, a.beta, za};
     const int64_t blocks = (int64_t)a.B * g.ntt * g.nnt;
-    hipLaunchKernelGGL(gate_logits_mfma, dim3((unsigned)blocks), dim3(kGWaves * 64), 0, s, p);
+    launch(gate_logits_mfma, dim3((unsigned)blocks), dim3(kGWaves * 64), 0, s, p);
   } else {
     const int64_t n = (int64_t)a.B * a.L * 2 * a.H;
     const dim3 grid((unsigned)((n + 255) / 256));
     if (a.dtype == 0)
-      hipLaunchKernelGGL(gate_logits_generic<bf16>, grid, dim3(256), 0, s, (const bf16 *)a.x,
+      launch(gate_logits_generic<bf16>, grid, dim3(256), 0, s, (const bf16 *)a.x,
                          (const bf16 *)a.Wa, (const bf16 *)a.Wb, a.B, a.L, a.D, a.H, a.beta, za);
     else
-      hipLaunchKernelGGL(gate_logits_generic<float>, grid, dim3(256), 0, s, (const float *)a.x,
+      launch(gate_logits_generic<float>, grid, dim3(256), 0, s, (const float *)a.x,
                          (const float *)a.Wa, (const float *)a.Wb, a.B, a.L, a.D, a.H, a.beta,
                          za);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbh = (int64_t)a.B * a.H;
-  hipLaunchKernelGGL(gate_alpha, dim3((unsigned)((nbh + 3) / 4)), dim3(256), 0, s, za, a.B, a.H,
+  launch(gate_alpha, dim3((unsigned)((nbh + 3) / 4)), dim3(256), 0, s, za, a.B, a.H,
                      a.L, g.nta, a.alpha);
   return hipGetLastError();
 }

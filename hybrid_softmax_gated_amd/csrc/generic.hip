@@ -157,7 +157,7 @@ template <typename T, int Dm>
 hipError_t gen_attention(const void *q, const void *k, const void *v, int B, int H, int Lq, int Lk,
                          float *o_intra, hipStream_t s) {
   dim3 grid((unsigned)((Lq + 63) / 64), (unsigned)H, (unsigned)B);
-  hipLaunchKernelGGL((gen_attn_kernel<T, Dm>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
+  launch((gen_attn_kernel<T, Dm>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
                      (const T *)v, H, Lq, Lk, o_intra);
   return hipGetLastError();
 }
@@ -166,7 +166,7 @@ template <typename T, int Dm>
 hipError_t gen_inter_combine(const void *q, const void *Wq, const float *S, const float *o_intra,
                              int B, int H, int L, void *out, bool with_inter, hipStream_t s) {
   dim3 grid((unsigned)((L + 63) / 64), (unsigned)H, (unsigned)B);
-  hipLaunchKernelGGL((gen_inter_combine_kernel<T, Dm>), grid, dim3(64), 0, s, (const T *)q,
+  launch((gen_inter_combine_kernel<T, Dm>), grid, dim3(64), 0, s, (const T *)q,
                      (const T *)Wq, S, o_intra, H, L, (T *)out, with_inter ? 1 : 0);
   return hipGetLastError();
 }
@@ -177,7 +177,7 @@ hipError_t gen_delta_partial(const void *k, const void *v, const void *Wk, const
                              hipStream_t s) {
   const int nchunk = (L + kGenChunk - 1) / kGenChunk;
   dim3 grid((unsigned)nchunk, (unsigned)H, (unsigned)B);
-  hipLaunchKernelGGL((gen_delta_partial_kernel<T, Dm>), grid, dim3(256), 0, s, (const T *)k,
+  launch((gen_delta_partial_kernel<T, Dm>), grid, dim3(256), 0, s, (const T *)k,
                      (const T *)v, (const T *)Wk, (const T *)Wv, S, beta, H, L, nchunk, ws_dS);
   return hipGetLastError();
 }

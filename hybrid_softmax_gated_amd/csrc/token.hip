@@ -675,7 +675,7 @@ template <typename T, int Dm>
 hipError_t tl_generic(const void *q, const void *k, const void *v, const void *W,
                       const float *o_intra, float *S, const float *alpha, const float *beta,
                       int B, int H, int L, int update, void *out, hipStream_t s) {
-  hipLaunchKernelGGL((tl_generic_kernel<T, Dm>), dim3((unsigned)H, (unsigned)B), dim3(Dm), 0, s,
+  launch((tl_generic_kernel<T, Dm>), dim3((unsigned)H, (unsigned)B), dim3(Dm), 0, s,
                      (const T *)q, (const T *)k, (const T *)v, (const T *)W, o_intra, S, alpha,
                      beta, H, L, update, (T *)out);
   return hipGetLastError();
@@ -691,7 +691,7 @@ hipError_t launch_token_level_bf16(const TokenLevelArgs &a, hipStream_t s) {
     PrepParams pp{(const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                   (const bf16 *)a.Wq, (const bf16 *)a.Wk, (const bf16 *)a.Wv,
                   a.alpha, a.beta, a.H, a.L, nchunk, nitems, per_xcd, (char *)a.records};
-    hipLaunchKernelGGL(tl_prep_kernel, dim3((unsigned)(8 * per_xcd)), dim3(512), 0, s, pp);
+    launch(tl_prep_kernel, dim3((unsigned)(8 * per_xcd)), dim3(512), 0, s, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -699,7 +699,7 @@ hipError_t launch_token_level_bf16(const TokenLevelArgs &a, hipStream_t s) {
   const int per_xcd = (nitems + 7) / 8;
   RecurParams rp{(const char *)a.records, a.alpha, a.S, a.o_inter, a.H, a.L, nchunk, nitems,
                  per_xcd, a.update};
-  hipLaunchKernelGGL(tl_recur_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, rp);
+  launch(tl_recur_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, rp);
   return hipGetLastError();
 }
 

@@ -297,16 +297,18 @@ ARL2_API arl2_status arl2_gate_projections(const void *x, const void *Wa, const 
                                            size_t ws_bytes, void *stream);
 
 /*
- * Kernel timing (diagnostics). While enabled, every kernel the library
- * launches is bracketed by a pair of hipEvents recorded on the launch stream.
- * A kernel that only reads its inputs and overwrites its outputs (all but
- * the in-place state update) is launched `repeat` times back to back inside
- * its pair, which spreads the events' own overhead over `repeat` launches;
- * the results are those of a single launch. repeat = 1 launches every kernel
- * once. arl2_profile_report waits for the recorded events and writes one
- * line per kernel, "<name> <launches> <total_ms>\n", into buf
- * (NUL-terminated, truncated to len). Disabled by default. Not for use under
- * graph capture.
+ * Kernel timing (diagnostics). While enabled, every launch (or pair of
+ * launches that one call makes for one step) is timed with a pair of
+ * hipEvents. With repeat = 1 the events are taken from the kernels' own
+ * start and end (hipExtLaunchKernel), so a time is that of the launch in its
+ * place in the call sequence, with no marker in between. With repeat > 1 a
+ * launch that only reads its inputs and overwrites its outputs (all but the
+ * in-place state update) is issued `repeat` times back to back between two
+ * event markers, which spreads the markers' own overhead over the repeats;
+ * the results are those of a single launch. arl2_profile_report waits for
+ * the recorded events and writes one line per launch kind,
+ * "<name> <launches> <total_ms>\n", into buf (NUL-terminated, truncated to
+ * len). Disabled by default. Not for use under graph capture.
  * Errors: INVALID_ARG for repeat outside [1, 1000], a NULL buf or len 0;
  * ARL2_ERR_HIP if an event cannot be created or queried.
  */

@@ -92,16 +92,18 @@ def test_workspace_bytes(B):
 @pytest.mark.parametrize("Bn,H,L", [(1, 12, 1560), (4, 12, 3600), (2, 3, 200), (3, 1, 1000),
                                     (1, 1, 64), (1, 2, 130), (8, 16, 777)])
 def test_bench_epilogue_bytes_follow_the_library_plan(B, Bn, H, L):
-    """bench.py prices the combine and delta launches with its own copy of
-    the attention plan; the library's workspace (partials, then the delta
-    contributions, each 256-byte aligned) must hold exactly those bytes."""
+    """bench.py reports the design's scratch bytes with its own copy of the
+    attention plan; the library's workspace (partials, then the delta
+    contributions, then the bf16 copy of the state, each 256-byte aligned)
+    must hold exactly those bytes."""
     import bench
 
     def al(x):
         return (x + 255) // 256 * 256
 
-    o_bytes, ml_bytes, ds = bench.workspace_parts(Bn, H, 128, L)
-    assert B.arl2_workspace_bytes(Bn, H, 128, L, B.ARL2_BF16) == al(o_bytes) + al(ml_bytes) + al(ds)
+    o_bytes, ml_bytes, ds, s16 = bench.workspace_parts(Bn, H, 128, L)
+    assert B.arl2_workspace_bytes(Bn, H, 128, L, B.ARL2_BF16) == (al(o_bytes) + al(ml_bytes) +
+                                                                  al(ds) + al(s16))
 
 
 FAKE_S = 0x7F0000000000

@@ -87,6 +87,27 @@ def measured_traffic(kernel, workload, digest):
     return t.get("bytes_per_launch")
 
 
+def launch_counters(workload):
+    """Per-launch counter figures (HBM bytes, MfmaUtil) from the committed
+    rocprofv3 summary of this workload, keyed by launch name, for the launches
+    whose sources are unchanged since; {} if there is none."""
+    path = os.path.join(ROOT, "profiles", f"frame_launches_{workload}_counters.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        t = json.load(f)
+    first = source_digest("attn.hip", "arl2_device.h", "delta_chunk.h")
+    second = source_digest("frame_tail.hip", "arl2_device.h")
+    ok = {"attn_partial": t["source_digests"]["first_launch"] == first,
+          "attn_delta": t["source_digests"]["first_launch"] == first,
+          "combine": t["source_digests"]["second_launch"] == second,
+          "combine_apply": t["source_digests"]["second_launch"] == second}
+    out = {k: v for k, v in t["launches"].items() if ok.get(k)}
+    if out:
+        out["mfma_loop_util_pct"] = t["mfma_loop_util_pct"]
+    return out
+
+
 def workspace_parts(B, H, d, L):
     """Bytes of the workspace regions one pass of the bf16 d = 128 path keeps
     between its launches: the key-range partials (bf16 O/l, then fp32 max
@@ -546,6 +567,7 @@ def main() -> int:
             "frac_of_measured_mfma_loop": round(att_tflops / mfma_loop, 4),
             "traffic_ratio": round(traffic / alg_bytes, 3) if traffic else None,
             "algorithmic_bytes": alg_bytes}
+        ctr = launch_counters(args.workload)
         if "attn_delta" in kern_us:
             dt = kern_us["attn_delta"] - att_us
             res["delta_update"] = {
@@ -558,17 +580,26 @@ def main() -> int:
                 "executed_tflops": round(2 * fc / (dt * 1e-6) / 1e12, 2) if dt > 0 else None,
                 "timing": "in sequence: the clean pass's first launch (attention + delta chunks) "
                           "minus the query-only pass's (attention alone)"}
+            if "attn_delta" in ctr and "attn_partial" in ctr:
+                res["delta_update"]["mfma_util_pct"] = {
+                    "attn_delta": ctr["attn_delta"]["mfma_util_pct"],
+                    "attn_partial": ctr["attn_partial"]["mfma_util_pct"],
+                    "pure_mfma_loop": ctr["mfma_loop_util_pct"],
+                    "source": "rocprofv3 MfmaUtil, committed counter summary of this workload"}
         epi = {}
         mb = method_bytes(B, H, d, L)
         for name in ("combine", "combine_apply"):
             if name in kern_us:
                 nbytes = mb[name]["method"]
                 gbs = nbytes / (kern_us[name] * 1e-6) / 1e9
+                tr = ctr.get(name, {}).get("bytes_per_launch")
                 epi[name] = {"bound": "hbm", "bytes": int(nbytes),
                              "scratch_bytes": int(mb[name]["scratch"]),
                              "avg_launch_us": round(kern_us[name], 2), "achieved": round(gbs, 1),
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": round(gbs / PEAK_HBM_GBS, 4)}
+                             "frac": round(gbs / PEAK_HBM_GBS, 4),
+                             "traffic": tr,
+                             "traffic_ratio": round(tr / nbytes, 3) if tr else None}
         res["epilogues"] = epi
     res["mfma_loop_peak_tflops"] = round(mfma_loop, 1)
     if extra is not None:

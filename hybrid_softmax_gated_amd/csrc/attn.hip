@@ -15,8 +15,11 @@
 // head's row of 128 values is 256 contiguous bytes and consecutive tokens of
 // one head are H*256 bytes apart.
 //
-// Attention items (one workgroup = 4 wavefronts = 128 queries of one head,
-// one contiguous key range; two workgroups per compute unit):
+// Attention items (one contiguous key range of one head; in the launch of
+// a clean pass 4 wavefronts = one block of 128 queries per workgroup, two
+// workgroups per compute unit, beside the update chunks; in every other
+// launch 8 wavefronts = two blocks of 128 queries sharing each K/V tile,
+// one workgroup per compute unit):
 //  * each wavefront keeps its 32 queries in registers as MFMA B operands and
 //    computes the transposed score tile S^T = K Q^T (keys on rows), so every
 //    lane owns one query: the row max and row sum of the online softmax are
@@ -68,19 +71,32 @@ __device__ __forceinline__ int item_of(int bid, int per_xcd) {
   return (bid & 7) * per_xcd + (bid >> 3);
 }
 
-// One attention item. Ks0/Ks1/Vs0/Vs1: double-buffered K and V tiles, each
-// its own LDS array so that the compiler sees the copies into one buffer and
-// the reads of the other as disjoint.
+// One attention item of a workgroup of NW wavefronts. NW = 4: one block of
+// 128 queries (item = stream, head, key range, query block). NW = 8: two
+// consecutive blocks over the same key range (item = stream, head, key
+// range, pair of blocks); wavefronts 4-7 take the second block, and all
+// eight share every K/V tile, which halves the tile copies per query.
+// Ks0/Ks1/Vs0/Vs1: double-buffered K and V tiles, each its own LDS array so
+// that the compiler sees the copies into one buffer and the reads of the
+// other as disjoint.
+template <int NW>
 __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *Ks0, char *Ks1,
                                           char *Vs0, char *Vs1) {
-  const int qblk = item % p.nqblk;
-  int rest = item / p.nqblk;
+  static_assert(NW == 4 || NW == 8, "wavefronts per workgroup");
+  const int nunit = NW == 4 ? p.nqblk : (p.nqblk + 1) / 2;
+  const int unit = item % nunit;
+  int rest = item / nunit;
   const int split = rest % p.nsplit;
   rest /= p.nsplit;
   const int h = rest % p.H, b = rest / p.H;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int waveN = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = NW == 4 ? waveN : waveN & 3;  // wavefront within its query block
+  const int qblk = NW == 4 ? unit : 2 * unit + (waveN >> 2);
+  // The second block of the last pair may lie past the frame: its
+  // wavefronts still copy tiles and meet every barrier, on zero queries.
+  const bool active = NW == 4 || qblk < p.nqblk;
   const int64_t tok = (int64_t)p.H * D;     // elements between tokens
   const int64_t tokB = tok * 2;             // bytes between tokens
   const bf16 *qbase = p.q + ((int64_t)b * p.Lq * p.H + h) * D;
@@ -89,13 +105,15 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
   const int kbeg = split == 0 ? 0 : p.kps0 + (split - 1) * p.kps;
   const int kend = min(p.Lk, split == 0 ? p.kps0 : kbeg + p.kps);
 
-  // Tile copies: wavefront w copies chunks 4w .. 4w+3 of 4 rows (1 KB) each;
-  // lane (r4 = l/16, pos = l%16) of chunk cc fetches row 4cc + r4, 16-byte
-  // unit pos ^ swizzle, so the bytes land in the swizzled layout.
-  int doff[4];
+  // Tile copies: the 16 chunks of 4 rows (1 KB) of a tile are shared out,
+  // CPW = 16 / NW per wavefront (chunks CPW*w .. CPW*w + CPW-1); lane
+  // (r4 = l/16, pos = l%16) of chunk cc fetches row 4cc + r4, 16-byte unit
+  // pos ^ swizzle, so the bytes land in the swizzled layout.
+  constexpr int CPW = 16 / NW;
+  int doff[CPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * (4 * wave + i) + (lane >> 4);
+  for (int i = 0; i < CPW; ++i) {
+    const int row = 4 * (CPW * waveN + i) + (lane >> 4);
     doff[i] = (int)(row * tokB) + 16 * ((lane & 15) ^ tile_swz(row & 15));
   }
   // Copy the tile starting at key t0 into (kt, vt); rows at or past kend
@@ -106,9 +124,9 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + t0 * tokB, n);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + t0 * tokB, n);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      buffer_to_lds16(rk, kt + (4 * wave + i) * 1024, doff[i]);
-      buffer_to_lds16(rv, vt + (4 * wave + i) * 1024, doff[i]);
+    for (int i = 0; i < CPW; ++i) {
+      buffer_to_lds16(rk, kt + (CPW * waveN + i) * 1024, doff[i]);
+      buffer_to_lds16(rv, vt + (CPW * waveN + i) * 1024, doff[i]);
     }
   };
 
@@ -242,6 +260,7 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
     if (!step(std::integral_constant<int, 1>(), t0 + KB)) break;
   }
 
+  if (!active) return;
   // Partial results: O / l of this key range in bf16, in register order
   // (one 16-byte unit per lane and (bb, r2): elements 4*(2*r2 + e2) + e of
   // o[bb], i.e. d_v = 32bb + 16*r2 + 8*e2 + 4*(l/32) + e), and (m, l) in
@@ -266,9 +285,11 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
   }
 }
 
-// S16 := bf16(S) (round to nearest even) for 2048 state values per item.
+// S16 := bf16(S) (round to nearest even) for 8 * NT state values per item
+// (NT threads per workgroup).
+template <int NT>
 __device__ __forceinline__ void state_copy_body(const float *S, bf16 *S16, int item) {
-  const int64_t i0 = (int64_t)item * 2048 + threadIdx.x * 8;
+  const int64_t i0 = ((int64_t)item * NT + threadIdx.x) * 8;
   const f32x4 a = *(const f32x4 *)(S + i0);
   const f32x4 c = *(const f32x4 *)(S + i0 + 4);
   bf16x8 t;
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void pass_head_kernel(PassKParams P) {
   int bid = blockIdx.x;
   if (bid < P.attn_blocks) {
     const int item = item_of(bid, P.a.per_xcd);
-    if (item < P.a.nitems) attn_body(P.a, item, Ks0, Ks1, Vs0, Vs1);
+    if (item < P.a.nitems) attn_body<4>(P.a, item, Ks0, Ks1, Vs0, Vs1);
     return;
   }
   bid -= P.attn_blocks;
@@ -315,7 +336,26 @@ __global__ __launch_bounds__(256, 2) void pass_head_kernel(PassKParams P) {
     return;
   }
   bid -= P.delta_blocks;
-  if (bid < P.copy_items) state_copy_body(P.S, P.S16, bid);
+  if (bid < P.copy_items) state_copy_body<256>(P.S, P.S16, bid);
+}
+
+// A launch with no update chunks (query-only passes, attention over a key
+// cache): eight wavefronts per workgroup, two query blocks per attention
+// item, one workgroup per compute unit; then the state copy, 4096 values
+// per workgroup.
+__global__ __launch_bounds__(512, 1) void attn8_kernel(PassKParams P) {
+  __shared__ __attribute__((aligned(1024))) char Ks0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ks1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Vs0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char Vs1[TILE_BYTES];
+  int bid = blockIdx.x;
+  if (bid < P.attn_blocks) {
+    const int item = item_of(bid, P.a.per_xcd);
+    if (item < P.a.nitems) attn_body<8>(P.a, item, Ks0, Ks1, Vs0, Vs1);
+    return;
+  }
+  bid -= P.attn_blocks;
+  if (bid < P.copy_items) state_copy_body<512>(P.S, P.S16, bid);
 }
 
 }  // namespace
@@ -339,7 +379,8 @@ AttnPlan plan_attention(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
   return pl;
 }
 
-static AttnKParams attn_params(const AttnArgs &a) {
+// Kernel parameters of the attention items, for workgroups of NW wavefronts.
+static AttnKParams attn_params(const AttnArgs &a, int nw) {
   AttnKParams p;
   p.q = (const bf16 *)a.q;
   p.k = (const bf16 *)a.k;
@@ -354,7 +395,8 @@ static AttnKParams attn_params(const AttnArgs &a) {
   p.ws_o = (char *)a.ws_o;
   p.ws_ml = a.ws_ml;
   p.scale = kLog2e / sqrtf((float)D);
-  p.nitems = a.B * a.H * a.plan.nsplit * a.plan.nqblk;
+  const int units = nw == 4 ? a.plan.nqblk : (a.plan.nqblk + 1) / 2;
+  p.nitems = a.B * a.H * a.plan.nsplit * units;
   p.per_xcd = (p.nitems + 7) / 8;
   return p;
 }
@@ -362,33 +404,44 @@ static AttnKParams attn_params(const AttnArgs &a) {
 hipError_t launch_pass_head_bf16(const AttnArgs &a, const DeltaArgs *d, const float *S, void *S16,
                                  int64_t state_values, hipStream_t s) {
   if (d && d->chunk != 96 && d->chunk != 128) return hipErrorInvalidValue;
-  if (S && state_values % 2048 != 0) return hipErrorInvalidValue;
   PassKParams P;
-  P.a = attn_params(a);
+  if (!d) {
+    // No update chunks: the eight-wavefront kernel.
+    if (S && state_values % 4096 != 0) return hipErrorInvalidValue;
+    P.a = attn_params(a, 8);
+    P.attn_blocks = 8 * P.a.per_xcd;
+    P.d = DeltaKParams{};
+    P.delta_blocks = 0;
+    P.per_xcd_d = 0;
+    P.S = S;
+    P.S16 = (bf16 *)S16;
+    P.copy_items = S ? (int)(state_values / 4096) : 0;
+    launch(attn8_kernel, dim3((unsigned)(P.attn_blocks + P.copy_items)), dim3(512), 0, s, P);
+    return hipGetLastError();
+  }
+  if (S && state_values % 2048 != 0) return hipErrorInvalidValue;
+  // With update chunks: four-wavefront workgroups, two per compute unit.
+  P.a = attn_params(a, 4);
   P.attn_blocks = 8 * P.a.per_xcd;
   P.d = DeltaKParams{};
-  P.delta_blocks = 0;
-  P.per_xcd_d = 0;
-  if (d) {
-    P.d.k = (const bf16 *)d->k;
-    P.d.v = (const bf16 *)d->v;
-    P.d.Wk = (const bf16 *)d->Wk;
-    P.d.Wv = (const bf16 *)d->Wv;
-    P.d.S = d->S;
-    P.d.beta = d->beta;
-    P.d.H = d->H;
-    P.d.L = d->L;
-    P.d.nchunk = d->nchunk;
-    P.d.nitems = d->B * d->H * d->nchunk;
-    P.d.ws_dS = d->ws_dS;
-    P.per_xcd_d = (P.d.nitems + 7) / 8;
-    P.delta_blocks = 8 * P.per_xcd_d;
-  }
+  P.d.k = (const bf16 *)d->k;
+  P.d.v = (const bf16 *)d->v;
+  P.d.Wk = (const bf16 *)d->Wk;
+  P.d.Wv = (const bf16 *)d->Wv;
+  P.d.S = d->S;
+  P.d.beta = d->beta;
+  P.d.H = d->H;
+  P.d.L = d->L;
+  P.d.nchunk = d->nchunk;
+  P.d.nitems = d->B * d->H * d->nchunk;
+  P.d.ws_dS = d->ws_dS;
+  P.per_xcd_d = (P.d.nitems + 7) / 8;
+  P.delta_blocks = 8 * P.per_xcd_d;
   P.S = S;
   P.S16 = (bf16 *)S16;
   P.copy_items = S ? (int)(state_values / 2048) : 0;
   const unsigned blocks = (unsigned)(P.attn_blocks + P.delta_blocks + P.copy_items);
-  if (d && d->chunk == 96)
+  if (d->chunk == 96)
     launch(pass_head_kernel<3>, dim3(blocks), dim3(256), 0, s, P);
   else
     launch(pass_head_kernel<4>, dim3(blocks), dim3(256), 0, s, P);

@@ -225,16 +225,23 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
       m = mnew;
     }
 
+    // Probabilities, rounded to bf16 for the MFMAs; the row sums add the
+    // fp32 values with plain VALU adds. (The bf16 dot-product instruction
+    // would sum the rounded values in half the instructions, but on gfx950
+    // it waits for the SIMD's matrix core, which the other wavefront keeps
+    // busy.) The two sums differ by at most 2^-9 relative, the bf16
+    // rounding step of the output itself, and by much less when many keys
+    // contribute (round-to-nearest-even errors have no bias).
     bf16x8 pb[4];
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pb[2 * sb + (i >> 3)][i & 7] = (bf16)exp2_fast(fmaf(s[sb][i], p.scale, -m));
-    // Row sums of the rounded probabilities (the values the MFMAs consume).
-    float ps[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) ps[kk] = sum_bf16x8(pb[kk], 0.f);
+      for (int i = 0; i < 16; ++i) {
+        const float e = exp2_fast(fmaf(s[sb][i], p.scale, -m));
+        pb[2 * sb + (i >> 3)][i & 7] = (bf16)e;
+        ps[2 * sb + (i >> 3)] += e;
+      }
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
     // O^T += V^T P^T over the tile's 64 keys (4 steps of 16).

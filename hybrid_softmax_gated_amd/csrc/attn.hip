@@ -71,6 +71,20 @@ __device__ __forceinline__ int item_of(int bid, int per_xcd) {
   return (bid & 7) * per_xcd + (bid >> 3);
 }
 
+// Waits until at most N vector-memory loads of this wavefront are in flight
+// (they complete in issue order), then meets the workgroup barrier. Unlike
+// __syncthreads, this adds no wait for the loads issued after those N.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // One attention item of a workgroup of NW wavefronts. NW = 4: one block of
 // 128 queries (item = stream, head, key range, query block). NW = 8: two
 // consecutive blocks over the same key range (item = stream, head, key
@@ -116,13 +130,22 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
     const int row = 4 * (CPW * waveN + i) + (lane >> 4);
     doff[i] = (int)(row * tokB) + 16 * ((lane & 15) ^ tile_swz(row & 15));
   }
-  // Copy the tile starting at key t0 into (kt, vt); rows at or past kend
-  // read as zeros.
-  auto copy_tile = [&](int t0, char *kt, char *vt) {
+  // Copy the K (or V) rows of the tile starting at key t0 into kt (vt):
+  // CPW loads per wavefront; rows at or past kend read as zeros.
+  // Bytes of K (or V) rows from key t0 to kend: 0 when t0 >= kend, so that
+  // a copy past the range issues its loads but reads nothing.
+  auto tile_bytes = [&](int t0) {
     const int64_t span = (int64_t)(kend - t0) * tokB;
-    const uint32_t n = (uint32_t)(span < (int64_t)0x7fffffff ? span : (int64_t)0x7fffffff);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + t0 * tokB, n);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + t0 * tokB, n);
+    return (uint32_t)(span <= 0 ? (int64_t)0 : span < (int64_t)0x7fffffff ? span : (int64_t)0x7fffffff);
+  };
+  auto copy_rows = [&](const char *base, int t0, char *dst) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + t0 * tokB, tile_bytes(t0));
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) buffer_to_lds16(r, dst + (CPW * waveN + i) * 1024, doff[i]);
+  };
+  auto copy_tile = [&](int t0, char *kt, char *vt) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + t0 * tokB, tile_bytes(t0));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + t0 * tokB, tile_bytes(t0));
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       buffer_to_lds16(rk, kt + (CPW * waveN + i) * 1024, doff[i]);
@@ -130,20 +153,21 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
     }
   };
 
-  // The wavefront's 32 queries as B operands: lane l holds query l%32,
-  // head-dim elements 16c + 8*(l/32) .. +7.
-  const int qrow = qblk * kQBlock + wave * 32 + l32;
+  // Loads of the first tile, in the order they are waited for: K (CPW
+  // copies), the wavefront's 32 queries (8 loads), V (CPW copies). Every
+  // wavefront issues all of them, so the in-order load counter tells
+  // when each group has landed. The queries become B operands: lane l
+  // holds query l%32, head-dim elements 16c + 8*(l/32) .. +7 (zeros past
+  // the frame).
+  copy_rows(kbase, kbeg, Ks0);
+  const int qrow0 = qblk * kQBlock + wave * 32;
+  const int qrows = max(0, min(32, p.Lq - qrow0));
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(qbase + (int64_t)qrow0 * tok, (uint32_t)qrows * (uint32_t)tokB);
   bf16x8 qop[8];
-  if (qrow < p.Lq) {
-    const bf16 *qp = qbase + qrow * tok + 8 * hl;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qop[c] = *(const bf16x8 *)(qp + 16 * c);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qop[c] = zero_bf16x8();
-  }
-
-  copy_tile(kbeg, Ks0, Vs0);
+  for (int c = 0; c < 8; ++c) qop[c] = buffer_load16(rq, l32 * (int)tokB + 32 * c + 16 * hl);
+  copy_rows(vbase, kbeg, Vs0);
 
   f32x16 o[4];
 #pragma unroll
@@ -168,17 +192,22 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
       voff[r][bb] = tile_off(row, col >> 3) + 2 * (col & 7);
     }
 
-  __builtin_amdgcn_s_waitcnt(0);  // Q operands and the first tile have landed
-  __syncthreads();
+  // Every wavefront's K copies of the first tile have landed; its queries
+  // and V copies may still be in flight.
+  vm_barrier<8 + CPW>();
 
   // One 64-key tile from buffer BUF; the next tile is copied into the other
   // buffer meanwhile. Returns false after the last tile.
-  auto step = [&](auto bufc, int t0) -> bool {
+  auto step = [&](auto bufc, auto firstc, int t0) -> bool {
     constexpr int BUF = decltype(bufc)::value;
+    constexpr bool FIRST = decltype(firstc)::value;
     const char *Kc = BUF ? Ks1 : Ks0;
     const char *Vc = BUF ? Vs1 : Vs0;
     const bool more = t0 + KB < kend;
-    if (more) copy_tile(t0 + KB, BUF ? Ks0 : Ks1, BUF ? Vs0 : Vs1);
+    // The first tile always issues the next copy (of zero rows if there is
+    // no next tile), so the number of loads in flight behind its own V
+    // copies does not depend on the range.
+    if (FIRST || more) copy_tile(t0 + KB, BUF ? Ks0 : Ks1, BUF ? Vs0 : Vs1);
     const int nvalid = kend - t0;
 
     // S^T for two 32-key sub-blocks (rows = keys, columns = this wave's
@@ -244,6 +273,10 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
       }
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
+    // The first tile's V copies of every wavefront have landed (the next
+    // tile's 2*CPW copies may not).
+    if constexpr (FIRST) vm_barrier<2 * CPW>();
+
     // O^T += V^T P^T over the tile's 64 keys (4 steps of 16).
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -262,9 +295,18 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
     return more;
   };
 
-  for (int t0 = kbeg;; t0 += 2 * KB) {
-    if (!step(std::integral_constant<int, 0>(), t0)) break;
-    if (!step(std::integral_constant<int, 1>(), t0 + KB)) break;
+  // The first tile has its own copy of the loop body, so that only its
+  // code waits for the queries and V copies one by one; the loop proper
+  // starts with everything landed.
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using First = std::true_type;
+  using Later = std::false_type;
+  if (step(B0(), First(), kbeg)) {
+    for (int t0 = kbeg + KB;; t0 += 2 * KB) {
+      if (!step(B1(), Later(), t0)) break;
+      if (!step(B0(), Later(), t0 + KB)) break;
+    }
   }
 
   if (!active) return;

@@ -140,6 +140,20 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void *
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, voff, 0, 0, 0);
 }
 
+// Waits until at most N vector-memory loads of this wavefront are in flight
+// (they complete in issue order), then meets the workgroup barrier. Unlike
+// __syncthreads, this adds no wait for the loads issued after those N.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Split an fp32 value into bf16 high and low parts, x ~= hi + lo (the
 // three-product bf16 scheme of Henry, Tang and Heinecke, ARITH 2019).
 __device__ __forceinline__ void split_bf16(float x, bf16 &hi, bf16 &lo) {

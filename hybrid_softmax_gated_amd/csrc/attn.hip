@@ -71,20 +71,6 @@ __device__ __forceinline__ int item_of(int bid, int per_xcd) {
   return (bid & 7) * per_xcd + (bid >> 3);
 }
 
-// Waits until at most N vector-memory loads of this wavefront are in flight
-// (they complete in issue order), then meets the workgroup barrier. Unlike
-// __syncthreads, this adds no wait for the loads issued after those N.
-template <int N>
-__device__ __forceinline__ void vm_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // One attention item of a workgroup of NW wavefronts. NW = 4: one block of
 // 128 queries (item = stream, head, key range, query block). NW = 8: two
 // consecutive blocks over the same key range (item = stream, head, key
@@ -160,6 +146,7 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
   // holds query l%32, head-dim elements 16c + 8*(l/32) .. +7 (zeros past
   // the frame).
   copy_rows(kbase, kbeg, Ks0);
+  __builtin_amdgcn_sched_barrier(0);  // keep the three groups in this order
   const int qrow0 = qblk * kQBlock + wave * 32;
   const int qrows = max(0, min(32, p.Lq - qrow0));
   const __amdgpu_buffer_rsrc_t rq =
@@ -167,6 +154,7 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
   bf16x8 qop[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) qop[c] = buffer_load16(rq, l32 * (int)tokB + 32 * c + 16 * hl);
+  __builtin_amdgcn_sched_barrier(0);
   copy_rows(vbase, kbeg, Vs0);
 
   f32x16 o[4];

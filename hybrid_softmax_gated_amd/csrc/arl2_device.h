@@ -67,8 +67,29 @@ __device__ __forceinline__ bool wave_any(bool p) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Exchange with the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// x of lane l and x of lane l ^ 32 (the other half of the wavefront), on
+// every lane, with one VALU lane swap (gfx950 v_permlane32_swap on two
+// copies of x) instead of a cross-lane read through the LDS unit, which
+// would queue behind the tile reads.
+__device__ __forceinline__ void halves_pair(float x, float &a, float &b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+// max and sum of x over lanes l and l ^ 32 (the same value on both; a sum
+// of two terms does not depend on their order).
+__device__ __forceinline__ float halves_max(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return a + b;
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -230,7 +230,7 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-    mx = fmaxf(mx, swap_halves(mx)) * p.scale;
+    mx = halves_max(mx) * p.scale;
     if (wave_any(mx > m + 8.f)) {
       const float mnew = fmaxf(m, mx);
       const float r = exp2_fast(m - mnew);
@@ -303,7 +303,7 @@ __device__ __forceinline__ void attn_body(const AttnKParams &p, int item, char *
   // o[bb], i.e. d_v = 32bb + 16*r2 + 8*e2 + 4*(l/32) + e), and (m, l) in
   // fp32 per query for the merge.
   const int64_t blk = (((int64_t)b * p.H + h) * p.nqblk + qblk) * p.nsplit + split;
-  const float lt = lsum + swap_halves(lsum);
+  const float lt = halves_sum(lsum);
   const float il = 1.f / lt;
   char *wo = p.ws_o + blk * kPartialOBytes + (wave * 8 * 64 + lane) * 16;
 #pragma unroll

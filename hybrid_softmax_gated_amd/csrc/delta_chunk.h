@@ -154,7 +154,7 @@ __device__ __forceinline__ void delta_body(const DeltaKParams p, int item, Split
     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) ss = fmaf(kt[bb][i], kt[bb][i], ss);
-    ss += swap_halves(ss);
+    ss = halves_sum(ss);
     inv = 1.f / fmaxf(sqrtf(ss), kL2Eps);
   }
   // W_v[d_in][d_v] for this wave's columns as B operands (k = d_in).

@@ -160,7 +160,7 @@ __device__ __forceinline__ void combine_body(const CombineKParams p, int item, c
     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) ss = fmaf(qp4[bb][i], qp4[bb][i], ss);
-    ss += swap_halves(ss);
+    ss = halves_sum(ss);
     const float inv = 1.f / fmaxf(sqrtf(ss), kL2Eps);
     // acc += O_inter^T = S^T Q'^T with Q' fed from the accumulators:
     // register 8*(g%2) + j of block g/2 holds feature 16g +

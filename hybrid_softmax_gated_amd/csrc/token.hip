@@ -176,7 +176,7 @@ __global__ __launch_bounds__(512) void tl_prep_kernel(PrepParams p) {
       for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) ss = fmaf(a0[bb][i], a0[bb][i], ss);
-      ss += swap_halves(ss);
+      ss = halves_sum(ss);
       s0 = 1.f / fmaxf(sqrtf(ss), kL2Eps);
     }
   }

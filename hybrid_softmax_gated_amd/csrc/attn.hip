@@ -23,16 +23,17 @@
 //  * each wavefront keeps its 32 queries in registers as MFMA B operands and
 //    computes the transposed score tile S^T = K Q^T (keys on rows), so every
 //    lane owns one query: the row max and row sum of the online softmax are
-//    in-register reductions plus one exchange between the wave halves;
+//    in-register reductions plus one VALU lane swap between the wave halves;
 //  * K and V tiles of 64 keys are staged in LDS row-major with a 16-byte
 //    XOR swizzle (no bank conflicts for either read pattern); V is read as
 //    the A operand of O^T = V^T P^T with the LDS transpose read, in the key
 //    order that lets the softmax probabilities leave the score accumulators
 //    and enter the next MFMA as its B operand with no data movement;
-//  * double-buffered tiles: the next tile's buffer loads are issued before
-//    the current tile's MFMAs and written to LDS after them (one barrier per
-//    tile); the loop is unrolled by two so every LDS address is a constant
-//    offset from a per-lane register;
+//  * double-buffered tiles: the next tile's buffer->LDS copies are issued
+//    before the current tile's MFMAs and waited for at the tile's end (one
+//    barrier per tile); the first tile waits only for its K copies before
+//    its scores and for its V copies before P.V; the loop is unrolled by two
+//    so every LDS address is a constant offset from a per-lane register;
 //  * per key range it writes O/l in bf16, in the accumulators' register
 //    order (16-byte coalesced stores), and the row max (log2 domain) and row
 //    sum in fp32.
